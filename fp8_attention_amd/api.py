@@ -1,0 +1,200 @@
+"""Python binding of libdm: argument marshalling only.
+
+Every step of the attention path runs in the library's HIP kernels; this
+module only allocates output tensors with PyTorch (device memory), passes raw
+pointers and the current HIP stream through ctypes, and raises on a non-OK
+status.  Names follow the C ABI in include/dm_attn.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+from typing import NamedTuple, Optional
+
+import torch
+
+from . import _lib
+
+MODES = {"stale": _lib.DM_DELTA_STALE, "do_matched": _lib.DM_DELTA_DO_MATCHED, "matched": _lib.DM_DELTA_MATCHED}
+FORMATS = {"e4m3": _lib.DM_E4M3, "e5m2": _lib.DM_E5M2}
+AXES = {"cols": _lib.DM_AXIS_COLS, "rows": _lib.DM_AXIS_ROWS}
+# operand -> FP8 format: E4M3 forward operands, E5M2 gradients
+OPERAND_FORMAT = {"q": "e4m3", "k": "e4m3", "v": "e4m3", "do": "e5m2"}
+
+
+class Fp8Operand(NamedTuple):
+    codes: torch.Tensor    # uint8
+    scales: torch.Tensor   # float32 powers of two, one per 32 codes
+
+    def c(self) -> _lib.Operand:
+        return _lib.Operand(self.codes.data_ptr(), self.scales.data_ptr())
+
+
+_NULL_OPERAND = _lib.Operand(None, None)
+
+
+@dataclasses.dataclass(frozen=True)
+class AttnShape:
+    batch: int
+    heads_q: int
+    heads_kv: int
+    seqlen: int
+    d_qk: int
+    d_v: int
+    causal: bool
+    softmax_scale: Optional[float] = None
+
+    @property
+    def sigma(self) -> float:
+        """The float32 value of the softmax scale the kernels use."""
+        s = self.softmax_scale if self.softmax_scale is not None else 1.0 / math.sqrt(self.d_qk)
+        return float(torch.tensor(s, dtype=torch.float32))
+
+    def c(self) -> _lib.Shape:
+        return _lib.Shape(self.batch, self.heads_q, self.heads_kv, self.seqlen, self.d_qk, self.d_v,
+                          int(bool(self.causal)), self.sigma)
+
+
+def padded_len(L: int) -> int:
+    return int(_lib.load().dm_padded_len(int(L)))
+
+
+def _stream(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def quantize(x: torch.Tensor, axis: str = "cols", fmt: str = "e4m3", rows_out: Optional[int] = None) -> Fp8Operand:
+    """dm_quantize_blockfp8 over the last two dims of x ([..., rows, cols], bf16 or float32).
+
+    axis="cols": codes [..., rows_out, cols], scales [..., rows_out, cols/32].
+    axis="rows": codes [..., cols, rows_out], scales [..., cols, rows_out/32] (transposed).
+    """
+    _need(x, "x")
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("x must be bfloat16 or float32")
+    *lead, rows, cols = x.shape
+    batch = 1
+    for n in lead:
+        batch *= n
+    rows_out = rows if rows_out is None else int(rows_out)
+    if axis == "cols":
+        codes = torch.empty((*lead, rows_out, cols), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((*lead, rows_out, max(cols // 32, 1)), dtype=torch.float32, device=x.device)
+    elif axis == "rows":
+        codes = torch.empty((*lead, cols, rows_out), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((*lead, cols, max(rows_out // 32, 1)), dtype=torch.float32, device=x.device)
+    else:
+        raise ValueError(f"axis must be 'cols' or 'rows', got {axis!r}")
+    dt = _lib.DM_BF16 if x.dtype == torch.bfloat16 else _lib.DM_F32
+    st = _lib.load().dm_quantize_blockfp8(x.data_ptr(), dt, batch, rows, cols, rows_out, AXES[axis], FORMATS[fmt],
+                                          codes.data_ptr(), scales.data_ptr(), _stream(x))
+    _lib.check(st, "dm_quantize_blockfp8")
+    return Fp8Operand(codes, scales)
+
+
+def quantize_operands(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, do: torch.Tensor) -> dict:
+    """The eight FP8 operands of the path, padded to dm_padded_len(L).
+
+    X_c: blocks along channels, codes [B, H, Lp, d]; X_s: blocks along the
+    sequence, transposed, codes [B, H, d, Lp].
+    """
+    L = q.shape[-2]
+    Lp = padded_len(L)
+    out = {}
+    for name, x in (("q", q), ("k", k), ("v", v), ("do", do)):
+        fmt = OPERAND_FORMAT[name]
+        out[name + "_c"] = quantize(x, "cols", fmt, Lp)
+        out[name + "_s"] = quantize(x, "rows", fmt, Lp)
+    return out
+
+
+def attn_fwd(shape: AttnShape, q_c: Fp8Operand, k_c: Fp8Operand, v_s: Fp8Operand,
+             o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """dm_attn_fwd -> (O [B,Hq,L,d_v] float32, LSE [B,Hq,L] float32)."""
+    dev = q_c.codes.device
+    B, Hq, L = shape.batch, shape.heads_q, shape.seqlen
+    if o is None:
+        o = torch.empty((B, Hq, L, shape.d_v), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
+    cs = shape.c()
+    st = _lib.load().dm_attn_fwd(ctypes.byref(cs), q_c.c(), k_c.c(), v_s.c(), o.data_ptr(), lse.data_ptr(),
+                                 _stream(q_c.codes))
+    _lib.check(st, "dm_attn_fwd")
+    return o, lse
+
+
+def attn_delta(shape: AttnShape, mode: str, *, o: Optional[torch.Tensor] = None, do: Optional[torch.Tensor] = None,
+               do_c: Optional[Fp8Operand] = None, q_c: Optional[Fp8Operand] = None,
+               k_c: Optional[Fp8Operand] = None, v_c: Optional[Fp8Operand] = None,
+               lse: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dm_attn_delta in mode "stale" (o, do), "do_matched" (o, do_c) or "matched" (do_c, q_c, k_c, v_c, lse)."""
+    if mode not in MODES:
+        raise ValueError(f"unknown delta mode {mode!r}")
+    ref = next(t for t in (o, lse, do, None if do_c is None else do_c.codes) if t is not None)
+    if out is None:
+        out = torch.empty((shape.batch, shape.heads_q, shape.seqlen), dtype=torch.float32, device=ref.device)
+    if do is not None:
+        _need(do, "do", torch.bfloat16)
+    cs = shape.c()
+    opc = lambda x: _NULL_OPERAND if x is None else x.c()  # noqa: E731
+    st = _lib.load().dm_attn_delta(ctypes.byref(cs), MODES[mode], _ptr(o), _ptr(do), opc(do_c), opc(q_c),
+                                   opc(k_c), opc(v_c), _ptr(lse), out.data_ptr(), _stream(ref))
+    _lib.check(st, "dm_attn_delta")
+    return out
+
+
+def attn_bwd(shape: AttnShape, ops: dict, lse: torch.Tensor, delta: torch.Tensor, probe: bool = False,
+             dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+             dv: Optional[torch.Tensor] = None) -> dict:
+    """dm_attn_bwd -> {"dq","dk","dv"} float32 (+ "rowsum","rowabs" float64 probes when probe=True)."""
+    dev = lse.device
+    B, Hq, Hkv, L = shape.batch, shape.heads_q, shape.heads_kv, shape.seqlen
+    if dq is None:
+        dq = torch.empty((B, Hq, L, shape.d_qk), dtype=torch.float32, device=dev)
+    if dk is None:
+        dk = torch.empty((B, Hkv, L, shape.d_qk), dtype=torch.float32, device=dev)
+    if dv is None:
+        dv = torch.empty((B, Hkv, L, shape.d_v), dtype=torch.float32, device=dev)
+    ps = pa = None
+    if probe:
+        ps = torch.empty((B, Hq, L), dtype=torch.float64, device=dev)
+        pa = torch.empty((B, Hq, L), dtype=torch.float64, device=dev)
+    cs = shape.c()
+    st = _lib.load().dm_attn_bwd(ctypes.byref(cs), ops["q_c"].c(), ops["q_s"].c(), ops["k_c"].c(), ops["k_s"].c(),
+                                 ops["v_c"].c(), ops["do_c"].c(), ops["do_s"].c(), lse.data_ptr(), delta.data_ptr(),
+                                 dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _ptr(ps), _ptr(pa), _stream(lse))
+    _lib.check(st, "dm_attn_bwd")
+    out = {"dq": dq, "dk": dk, "dv": dv}
+    if probe:
+        out["rowsum"], out["rowabs"] = ps, pa
+    return out
+
+
+def fwd_delta_bwd(shape: AttnShape, ops: dict, mode: str = "matched", do: Optional[torch.Tensor] = None,
+                  probe: bool = False) -> dict:
+    """One pass of the whole path on already-quantized operands: forward, delta, backward."""
+    o, lse = attn_fwd(shape, ops["q_c"], ops["k_c"], ops["v_s"])
+    if mode == "matched":
+        d = attn_delta(shape, mode, do_c=ops["do_c"], q_c=ops["q_c"], k_c=ops["k_c"], v_c=ops["v_c"], lse=lse)
+    elif mode == "do_matched":
+        d = attn_delta(shape, mode, o=o, do_c=ops["do_c"])
+    else:
+        d = attn_delta(shape, mode, o=o, do=do)
+    g = attn_bwd(shape, ops, lse, d, probe=probe)
+    g.update(o=o, lse=lse, delta=d)
+    return g

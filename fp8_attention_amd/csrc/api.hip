@@ -1,0 +1,143 @@
+// C ABI of libdm: argument validation (pure host code, no HIP call before it
+// passes) and dispatch to the kernel launchers.
+#include <math.h>
+#include <stdint.h>
+
+#include "dm_attn.h"
+#include "dm_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+dm_status check_shape(const dm_attn_shape* s) {
+  if (!s) return DM_ERR_NULL;
+  if (s->batch < 1 || s->heads_q < 1 || s->heads_kv < 1 || s->seqlen < 0) return DM_ERR_SHAPE;
+  if (s->batch > 65535 || s->heads_q > 65535 || s->seqlen > (1 << 26)) return DM_ERR_SHAPE;
+  if (s->heads_q % s->heads_kv != 0) return DM_ERR_SHAPE;
+  if (s->d_qk != 64 && s->d_qk != 128 && s->d_qk != 192) return DM_ERR_SHAPE;
+  if (s->d_v != 64 && s->d_v != 128) return DM_ERR_SHAPE;
+  if (s->causal != 0 && s->causal != 1) return DM_ERR_SHAPE;
+  if (!(s->softmax_scale > 0.f) || !isfinite(s->softmax_scale)) return DM_ERR_SHAPE;
+  return DM_OK;
+}
+
+dm_status check_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!p) return DM_ERR_NULL;
+  for (const void* p : ps)
+    if (!aligned16(p)) return DM_ERR_ALIGN;
+  return DM_OK;
+}
+
+dm_status check_operand(const dm_fp8_operand& op) { return check_ptrs({op.codes, op.scales}); }
+
+dm::AttnDims dims_of(const dm_attn_shape* s) {
+  dm::AttnDims d;
+  d.B = s->batch;
+  d.Hq = s->heads_q;
+  d.Hkv = s->heads_kv;
+  d.L = s->seqlen;
+  d.Lp = (int)dm_padded_len(s->seqlen);
+  d.dqk = s->d_qk;
+  d.dv = s->d_v;
+  d.causal = s->causal;
+  d.sigma = s->softmax_scale;
+  return d;
+}
+
+dm::Operand op(const dm_fp8_operand& o) { return dm::Operand{o.codes, o.scales}; }
+
+dm_status hip_status(hipError_t e) { return e == hipSuccess ? DM_OK : DM_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t dm_padded_len(int64_t L) {
+  if (L < 0) return -1;
+  return (L + 127) / 128 * 128;
+}
+
+const char* dm_status_string(dm_status s) {
+  switch (s) {
+    case DM_OK: return "DM_OK";
+    case DM_ERR_NULL: return "DM_ERR_NULL: a required pointer is NULL";
+    case DM_ERR_SHAPE: return "DM_ERR_SHAPE: unsupported or inconsistent sizes";
+    case DM_ERR_ALIGN: return "DM_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case DM_ERR_ENUM: return "DM_ERR_ENUM: an enum argument is out of range";
+    case DM_ERR_HIP: return "DM_ERR_HIP: the HIP runtime reported an error";
+  }
+  return "unknown dm_status";
+}
+
+dm_status dm_quantize_blockfp8(const void* x, dm_dtype dtype, int64_t batch, int64_t rows, int64_t cols,
+                               int64_t rows_out, dm_block_axis axis, dm_fp8_format fmt, uint8_t* codes,
+                               float* scales, hipStream_t stream) {
+  if ((int)dtype != DM_BF16 && (int)dtype != DM_F32) return DM_ERR_ENUM;
+  if ((int)axis != DM_AXIS_COLS && (int)axis != DM_AXIS_ROWS) return DM_ERR_ENUM;
+  if ((int)fmt != DM_E4M3 && (int)fmt != DM_E5M2) return DM_ERR_ENUM;
+  if (batch < 1 || rows < 0 || cols < 32 || cols % 32 != 0 || rows_out < rows) return DM_ERR_SHAPE;
+  if (batch > 65535 || rows_out > ((int64_t)1 << 36) || cols > (1 << 20)) return DM_ERR_SHAPE;
+  if (axis == DM_AXIS_ROWS && rows_out % 32 != 0) return DM_ERR_SHAPE;
+  dm_status st = check_ptrs({x, codes, scales});
+  if (st != DM_OK) return st;
+  if (rows_out == 0) return DM_OK;
+  return hip_status(dm::launch_quantize(x, (int)dtype, batch, rows, cols, rows_out, (int)axis, (int)fmt, codes,
+                                        scales, stream));
+}
+
+dm_status dm_attn_fwd(const dm_attn_shape* shape, dm_fp8_operand q_c, dm_fp8_operand k_c, dm_fp8_operand v_s,
+                      float* o, float* lse, hipStream_t stream) {
+  dm_status st = check_shape(shape);
+  if (st != DM_OK) return st;
+  if ((st = check_operand(q_c)) != DM_OK || (st = check_operand(k_c)) != DM_OK ||
+      (st = check_operand(v_s)) != DM_OK || (st = check_ptrs({o, lse})) != DM_OK)
+    return st;
+  if (shape->seqlen == 0) return DM_OK;
+  return hip_status(dm::launch_fwd(dims_of(shape), op(q_c), op(k_c), op(v_s), o, lse, stream));
+}
+
+dm_status dm_attn_delta(const dm_attn_shape* shape, dm_delta_mode mode, const float* o, const uint16_t* do_bf16,
+                        dm_fp8_operand do_c, dm_fp8_operand q_c, dm_fp8_operand k_c, dm_fp8_operand v_c,
+                        const float* lse, float* delta, hipStream_t stream) {
+  dm_status st = check_shape(shape);
+  if (st != DM_OK) return st;
+  if ((int)mode != DM_DELTA_STALE && (int)mode != DM_DELTA_DO_MATCHED && (int)mode != DM_DELTA_MATCHED)
+    return DM_ERR_ENUM;
+  if ((st = check_ptrs({delta})) != DM_OK) return st;
+  if (mode == DM_DELTA_STALE) {
+    if ((st = check_ptrs({o, do_bf16})) != DM_OK) return st;
+  } else if (mode == DM_DELTA_DO_MATCHED) {
+    if ((st = check_ptrs({o})) != DM_OK || (st = check_operand(do_c)) != DM_OK) return st;
+  } else {
+    if ((st = check_operand(do_c)) != DM_OK || (st = check_operand(q_c)) != DM_OK ||
+        (st = check_operand(k_c)) != DM_OK || (st = check_operand(v_c)) != DM_OK ||
+        (st = check_ptrs({lse})) != DM_OK)
+      return st;
+  }
+  if (shape->seqlen == 0) return DM_OK;
+  const dm::AttnDims d = dims_of(shape);
+  if (mode == DM_DELTA_MATCHED)
+    return hip_status(dm::launch_delta_matched(d, op(do_c), op(q_c), op(k_c), op(v_c), lse, delta, stream));
+  return hip_status(dm::launch_delta_rows(d, (int)mode, o, do_bf16, op(do_c), delta, stream));
+}
+
+dm_status dm_attn_bwd(const dm_attn_shape* shape, dm_fp8_operand q_c, dm_fp8_operand q_s, dm_fp8_operand k_c,
+                      dm_fp8_operand k_s, dm_fp8_operand v_c, dm_fp8_operand do_c, dm_fp8_operand do_s,
+                      const float* lse, const float* delta, float* dq, float* dk, float* dv,
+                      double* probe_rowsum_ds, double* probe_rowsum_abs_pdp, hipStream_t stream) {
+  dm_status st = check_shape(shape);
+  if (st != DM_OK) return st;
+  const dm_fp8_operand ops[7] = {q_c, q_s, k_c, k_s, v_c, do_c, do_s};
+  for (const auto& x : ops)
+    if ((st = check_operand(x)) != DM_OK) return st;
+  if ((st = check_ptrs({lse, delta, dq, dk, dv})) != DM_OK) return st;
+  if ((probe_rowsum_ds == nullptr) != (probe_rowsum_abs_pdp == nullptr)) return DM_ERR_NULL;
+  if (probe_rowsum_ds && (st = check_ptrs({probe_rowsum_ds, probe_rowsum_abs_pdp})) != DM_OK) return st;
+  if (shape->seqlen == 0) return DM_OK;
+  return hip_status(dm::launch_bwd(dims_of(shape), op(q_c), op(q_s), op(k_c), op(k_s), op(v_c), op(do_c),
+                                   op(do_s), lse, delta, dq, dk, dv, probe_rowsum_ds, probe_rowsum_abs_pdp, stream));
+}
+
+}  // extern "C"

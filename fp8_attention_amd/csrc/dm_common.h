@@ -1,0 +1,102 @@
+// Device helpers shared by the gfx950 kernels of libdm.
+//
+// Scaled FP8 matrix-core instruction (v_mfma_scale_f32_32x32x64_f8f6f4) lane
+// layout, as used throughout (lane l, R = l % 32, h = l / 32):
+//   A (32 x 64, row R): bytes 0..15 hold K-slots 16h+0..15 (K-block 0),
+//                       bytes 16..31 hold K-slots 32+16h+0..15 (K-block 1);
+//   B (64 x 32, col R): the same K-slot assignment;
+//   the E8M0 scale of (row R, K-block kb) comes from lane R + 32*kb, i.e. lane
+//   (R, h) supplies the scale of K-block h;
+//   C (32 x 32): register v of lane l holds row 8*(v/4) + 4*h + v%4, column R.
+// A K-block of 32 slots therefore spans the first (or second) 16 bytes of the
+// two lanes R and R+32, and one 32-element quantization block maps onto one
+// K-block when each lane of the pair holds 16 of its elements.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dm {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kBlock = 32;     // elements per scale block
+constexpr int kChunk = 128;    // keys per running-max update / tile length
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+enum Fmt : int { E4M3 = 0, E5M2 = 1 };
+
+// Fmax = 1.75 * 2^emax_shift: 448 = 1.75*2^8 (E4M3), 57344 = 1.75*2^15 (E5M2).
+template <int F> struct FmtTraits;
+template <> struct FmtTraits<E4M3> { static constexpr int emax = 8; };
+template <> struct FmtTraits<E5M2> { static constexpr int emax = 15; };
+
+// Smallest integer k with amax <= Fmax * 2^k, clamped to [-126, 127].
+// amax = 1.m * 2^e:  k = e - emax when 1.m <= 1.75, else e - emax + 1.
+// amax == 0 or subnormal gives e = -127 and clamps to -126.
+template <int F>
+__device__ __forceinline__ int scale_exp(float amax) {
+  uint32_t b = __float_as_uint(amax);
+  int e = (int)((b >> 23) & 0xff) - 127;
+  int k = e - FmtTraits<F>::emax + ((b & 0x7fffff) > 0x600000u ? 1 : 0);
+  return min(max(k, -126), 127);
+}
+
+__device__ __forceinline__ float exp2i(int k) {        // 2^k, k in [-126, 127]
+  return __uint_as_float((uint32_t)(k + 127) << 23);
+}
+
+// Pack four floats (already divided by the block scale, |x| <= Fmax) into one
+// dword of FP8 codes, byte i = code of x_i.  Round to nearest even.
+template <int F>
+__device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d) {
+  uint32_t w;
+  if constexpr (F == E4M3) {
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0u, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  } else {
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0u, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
+  }
+  return w;
+}
+
+// The other lane of a (l, l^32) pair: returns {x_lo_lane, x_hi_lane} ordered
+// so that max/sum of the two gives the pair reduction on both lanes.
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int FA, int FB>
+__device__ __forceinline__ v16f mfma(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, sa, 0, sb);
+}
+
+// E8M0 byte of a float32 power-of-two scale (its biased exponent).
+__device__ __forceinline__ int e8m0(float s) { return (int)(__float_as_uint(s) >> 23); }
+
+// Row index (within a 32-row MFMA tile) of the operand row that should hold
+// element 16*h + v of the lane pair (R, R+32) after the product: a C-layout
+// row 8a + 4b + c is loaded from element 16b + 4a + c.
+__device__ __forceinline__ int pair_row(int r) {
+  return ((r >> 2) & 1) * 16 + (r >> 3) * 4 + (r & 3);
+}
+
+__device__ __forceinline__ v8i cat(const v4i& lo, const v4i& hi) {
+  v8i r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+__device__ __forceinline__ v4i lds_read16(const uint8_t* p) { return *reinterpret_cast<const v4i*>(p); }
+
+}  // namespace dm

@@ -1,0 +1,36 @@
+// Internal launcher declarations shared by the API translation unit and the
+// kernel translation units of libdm.  Shapes reaching these functions have
+// already been validated by the API layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dm {
+
+struct AttnDims {
+  int B, Hq, Hkv, L, Lp, dqk, dv, causal;
+  float sigma;
+};
+
+struct Operand {
+  const uint8_t* codes;
+  const float* scales;
+};
+
+hipError_t launch_quantize(const void* x, int dtype, int64_t batch, int64_t rows, int64_t cols, int64_t rows_out,
+                           int axis, int fmt, uint8_t* codes, float* scales, hipStream_t s);
+
+hipError_t launch_fwd(const AttnDims& d, Operand q_c, Operand k_c, Operand v_s, float* o, float* lse, hipStream_t s);
+
+hipError_t launch_delta_rows(const AttnDims& d, int mode, const float* o, const uint16_t* do_bf16, Operand do_c,
+                             float* delta, hipStream_t s);
+hipError_t launch_delta_matched(const AttnDims& d, Operand do_c, Operand q_c, Operand k_c, Operand v_c,
+                                const float* lse, float* delta, hipStream_t s);
+
+hipError_t launch_bwd(const AttnDims& d, Operand q_c, Operand q_s, Operand k_c, Operand k_s, Operand v_c,
+                      Operand do_c, Operand do_s, const float* lse, const float* delta, float* dq, float* dk,
+                      float* dv, double* probe_sum, double* probe_abs, hipStream_t s);
+
+hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t s);
+
+}  // namespace dm

@@ -1,0 +1,130 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol, and
+rejects invalid arguments with the documented status before touching the GPU.
+
+Every call here carries at least one invalid argument, so none of them can
+reach a kernel launch even on a machine with a GPU.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from fp8_attention_amd import _lib
+from fp8_attention_amd.api import AttnShape
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dm_attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libdm.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(dm_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declarations_are_exported():
+    names = _declared()
+    assert set(names) == set(_lib.EXPORTS), names
+    lib = _lib.load()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    assert set(names) <= syms
+
+
+def test_padded_len_and_strings():
+    lib = _lib.load()
+    assert [lib.dm_padded_len(x) for x in (0, 1, 128, 129, 65536)] == [0, 128, 128, 256, 65536]
+    assert lib.dm_padded_len(-1) == -1
+    for s in range(6):
+        assert _lib.status_string(s).startswith("DM_")
+    assert "unknown" in _lib.status_string(99)
+
+
+FAKE = 0x1000          # aligned, never dereferenced: every call below fails validation first
+MIS = 0x1004
+
+
+def _op(p=FAKE, q=FAKE):
+    return _lib.Operand(p, q)
+
+
+def _fwd(shape, q=None, o=FAKE, lse=FAKE):
+    lib = _lib.load()
+    s = shape.c() if isinstance(shape, AttnShape) else shape
+    return lib.dm_attn_fwd(ctypes.byref(s) if s is not None else None, q or _op(), _op(), _op(), o, lse, None)
+
+
+BAD_SHAPES = [
+    AttnShape(1, 3, 2, 128, 128, 128, True),       # Hq % Hkv != 0
+    AttnShape(1, 2, 2, 128, 96, 128, True),        # unsupported d_qk
+    AttnShape(1, 2, 2, 128, 128, 192, True),       # unsupported d_v
+    AttnShape(0, 2, 2, 128, 128, 128, True),       # empty batch
+    AttnShape(1, 2, 2, -5, 128, 128, True),        # negative length
+    AttnShape(1, 2, 2, 128, 128, 128, True, -1.0),  # non-positive scale
+    AttnShape(1, 2, 2, 128, 128, 128, True, float("nan")),
+    AttnShape(1, 2, 2, (1 << 26) + 1, 128, 128, True),
+]
+
+
+@pytest.mark.parametrize("shape", BAD_SHAPES)
+def test_bad_shapes(shape):
+    assert _fwd(shape) == _lib.DM_ERR_SHAPE
+
+
+def test_bad_causal_flag_and_null_shape():
+    s = AttnShape(1, 2, 2, 128, 128, 128, True).c()
+    s.causal = 2
+    assert _fwd(s) == _lib.DM_ERR_SHAPE
+    assert _fwd(None) == _lib.DM_ERR_NULL
+
+
+def test_null_and_misaligned_pointers():
+    # a NULL output with an otherwise valid call is caught; so is a misaligned one
+    good = AttnShape(1, 2, 2, 128, 128, 128, True)
+    assert _fwd(good, o=None) == _lib.DM_ERR_NULL
+    assert _fwd(good, q=_op(FAKE, None)) == _lib.DM_ERR_NULL
+    assert _fwd(good, lse=MIS) == _lib.DM_ERR_ALIGN
+    assert _fwd(good, q=_op(MIS, FAKE)) == _lib.DM_ERR_ALIGN
+
+
+def test_delta_mode_and_required_pointers():
+    lib = _lib.load()
+    s = AttnShape(1, 2, 2, 128, 128, 128, True).c()
+    n = _lib.Operand(None, None)
+    assert lib.dm_attn_delta(ctypes.byref(s), 7, FAKE, FAKE, n, n, n, n, FAKE, FAKE, None) == _lib.DM_ERR_ENUM
+    # stale needs o and dO; matched needs the four operands and lse
+    assert lib.dm_attn_delta(ctypes.byref(s), 0, None, FAKE, n, n, n, n, None, FAKE, None) == _lib.DM_ERR_NULL
+    assert lib.dm_attn_delta(ctypes.byref(s), 1, FAKE, None, n, n, n, n, None, FAKE, None) == _lib.DM_ERR_NULL
+    assert lib.dm_attn_delta(ctypes.byref(s), 2, None, None, _op(), _op(), _op(), n, FAKE, FAKE,
+                             None) == _lib.DM_ERR_NULL
+    assert lib.dm_attn_delta(ctypes.byref(s), 2, None, None, _op(), _op(), _op(), _op(), None, FAKE,
+                             None) == _lib.DM_ERR_NULL
+
+
+def test_bwd_probe_pointers_come_in_pairs():
+    lib = _lib.load()
+    s = AttnShape(1, 2, 2, 128, 128, 128, True).c()
+    ops = [_op()] * 7
+    assert lib.dm_attn_bwd(ctypes.byref(s), *ops, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == _lib.DM_ERR_NULL
+    assert lib.dm_attn_bwd(ctypes.byref(s), *ops, FAKE, FAKE, FAKE, FAKE, FAKE, MIS, MIS, None) == _lib.DM_ERR_ALIGN
+    s.d_v = 32
+    assert lib.dm_attn_bwd(ctypes.byref(s), *ops, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None) == _lib.DM_ERR_SHAPE
+
+
+def test_quantize_validation():
+    lib = _lib.load()
+    q = lib.dm_quantize_blockfp8
+    assert q(FAKE, 2, 1, 64, 64, 64, 0, 0, FAKE, FAKE, None) == _lib.DM_ERR_ENUM      # dtype
+    assert q(FAKE, 0, 1, 64, 64, 64, 5, 0, FAKE, FAKE, None) == _lib.DM_ERR_ENUM      # axis
+    assert q(FAKE, 0, 1, 64, 64, 64, 0, 3, FAKE, FAKE, None) == _lib.DM_ERR_ENUM      # format
+    assert q(FAKE, 0, 1, 64, 48, 64, 0, 0, FAKE, FAKE, None) == _lib.DM_ERR_SHAPE     # cols % 32
+    assert q(FAKE, 0, 1, 64, 64, 32, 0, 0, FAKE, FAKE, None) == _lib.DM_ERR_SHAPE     # rows_out < rows
+    assert q(FAKE, 0, 1, 64, 64, 80, 1, 0, FAKE, FAKE, None) == _lib.DM_ERR_SHAPE     # rows_out % 32 (rows axis)
+    assert q(FAKE, 0, 0, 64, 64, 64, 0, 0, FAKE, FAKE, None) == _lib.DM_ERR_SHAPE     # batch
+    assert q(None, 0, 1, 64, 64, 64, 0, 0, FAKE, FAKE, None) == _lib.DM_ERR_NULL
+    assert q(FAKE, 0, 1, 64, 64, 64, 0, 0, FAKE, MIS, None) == _lib.DM_ERR_ALIGN

@@ -1,0 +1,318 @@
+"""GPU parity of libdm against the CPU oracle (run with ``-m gpu`` on an MI355X).
+
+Bar (per tensor): FP8 codes and scales bit-exact; O, dQ, dK, dV within
+2e-3 x RMS(oracle) elementwise, plus the first-order radius of in-kernel casts
+whose exact input lies within FP32 rounding of a rounding or scale boundary
+(both casts are correct there); LSE and delta within their FP32 rounding
+budget; under Delta-Matching |sum_j dS_ij| <= 1e-5 sum_j |P_ij dP_ij| on the
+kernel's own pre-cast dS.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from fp8_attention_amd import workloads as W
+from oracle import attention as A
+from oracle import fp8
+from tests import parity_util as U
+
+pytestmark = pytest.mark.gpu
+
+MODES = ("stale", "do_matched", "matched")
+
+
+def _api():
+    from fp8_attention_amd import api
+    return api
+
+
+def _log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+SMALL = {
+    # the tiny single-head workload exactly
+    "tiny": W.WORKLOADS["tiny"],
+    # GQA, causal, ragged length (2.5 tiles), RMSNorm'd Q/K
+    "gqa_ragged": W.small("gqa_ragged", batch=2, heads_q=4, heads_kv=2, seqlen=320, d_qk=128, d_v=128,
+                          causal=True, kind="rmsnorm", seed=11),
+    # near-saturated rows (channel-7 gains of the long-context workload)
+    "gqa_gain": W.small("gqa_gain", batch=1, heads_q=4, heads_kv=1, seqlen=384, d_qk=128, d_v=128, causal=True,
+                        kind="rmsnorm", q_gain7=2.0, k_gain7=5.4, seed=12),
+    # MLA-shaped head dims
+    "mla": W.small("mla", batch=1, heads_q=2, heads_kv=2, seqlen=200, d_qk=192, d_v=128, causal=True,
+                   kind="scaled", seed=13),
+    # non-causal, mixed head dims, ragged
+    "mixed_nc": W.small("mixed_nc", batch=1, heads_q=2, heads_kv=1, seqlen=257, d_qk=64, d_v=128, causal=False,
+                        kind="iid", seed=14),
+}
+
+
+@functools.lru_cache(maxsize=None)
+def _case(name):
+    w = SMALL[name]
+    inputs = W.generate(w)
+    api = _api()
+    shape = api.AttnShape(w.batch, w.heads_q, w.heads_kv, w.seqlen, w.d_qk, w.d_v, w.causal)
+    shp = U.oracle_shape(w, shape.sigma)
+    _log(f"[oracle] {name}")
+    ref = U.run_oracle(inputs, shp, modes=MODES)
+    return w, inputs, shape, shp, ref
+
+
+def _gpu_ops(inputs):
+    api = _api()
+    dev = {n: t.cuda() for n, t in inputs.items()}
+    return dev, api.quantize_operands(dev["q"], dev["k"], dev["v"], dev["do"])
+
+
+def _f32(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+# ---------------------------------------------------------------------------
+# quantize: bit-exact codes and scales
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_quantize_operands_bit_exact(name):
+    w, inputs, shape, shp, ref = _case(name)
+    _log(f"[quantize] {name}")
+    _, ops = _gpu_ops(inputs)
+    torch.cuda.synchronize()
+    L, Lp = w.seqlen, _api().padded_len(w.seqlen)
+    L32 = (L + 31) // 32 * 32
+    for key, (codes, scales) in ref["qops"].items():
+        g = ops[key]
+        gc, gs = g.codes.cpu().numpy(), g.scales.cpu().numpy().astype(np.float64)
+        if key.endswith("_c"):
+            assert np.array_equal(gc[..., :L, :], codes), key
+            assert np.array_equal(gs[..., :L, :], scales), key
+            assert not gc[..., L:, :].any() and np.all(gs[..., L:, :] == 2.0 ** -126), key
+        else:
+            assert np.array_equal(gc[..., :L32], codes), key
+            assert np.array_equal(gs[..., :L32 // 32], scales), key
+            assert not gc[..., L32:].any() and np.all(gs[..., L32 // 32:] == 2.0 ** -126), key
+    assert Lp % 128 == 0 and Lp >= L
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("axis", ["cols", "rows"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_quantize_special_values(fmt, axis, dtype):
+    """Zeros, bf16 subnormals, huge and tiny blocks, exact scale boundaries, negative zero."""
+    api = _api()
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((3, 96, 64)) * np.exp(rng.uniform(-30, 30, (3, 96, 1)))
+    x[0, :32] = 0.0                                     # all-zero blocks
+    x[0, 32:40] = -0.0
+    x[1, :8] = 1e-40                                    # subnormal in bf16/f32
+    x[1, 8:16, :32] = fp8.FORMATS[fmt].fmax * 2.0 ** 5  # amax exactly on a boundary
+    x[2, :4] = 3e38 if dtype == torch.float32 else 1e38
+    xt = torch.from_numpy(x).to(dtype)
+    xd = xt.double().numpy()
+    rows_out = 128
+    got = api.quantize(xt.cuda(), axis, fmt, rows_out)
+    torch.cuda.synchronize()
+    if axis == "cols":
+        xp = np.zeros((3, rows_out, 64))
+        xp[:, :96] = xd
+        codes, scales, _ = fp8.quantize_lastaxis(xp, fmt)
+    else:
+        xp = np.zeros((3, 64, rows_out))
+        xp[:, :, :96] = np.swapaxes(xd, 1, 2)
+        codes, scales, _ = fp8.quantize_lastaxis(xp, fmt)
+    assert np.array_equal(got.codes.cpu().numpy(), codes)
+    assert np.array_equal(got.scales.cpu().numpy().astype(np.float64), scales)
+
+
+# ---------------------------------------------------------------------------
+# forward, delta, backward, each against the oracle with the oracle's own upstream values
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_fwd_parity(name):
+    w, inputs, shape, shp, ref = _case(name)
+    _log(f"[fwd] {name}")
+    api = _api()
+    _, ops = _gpu_ops(inputs)
+    o, lse = api.attn_fwd(shape, ops["q_c"], ops["k_c"], ops["v_s"])
+    torch.cuda.synchronize()
+    f = ref["fwd"]
+    s = U.compare("O", o, f["o"], radius=f["r_o"])
+    lse_tol = A.TAU * (np.abs(f["lse"]) + 1.0)
+    U.compare("LSE", lse, f["lse"], radius=lse_tol, rel=0.0)
+    _log(f"   {s} flagged casts {f['n_flag']} blocks {f['n_block_flag']}")
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("name", list(SMALL))
+def test_delta_parity(name, mode):
+    w, inputs, shape, shp, ref = _case(name)
+    _log(f"[delta] {name} {mode}")
+    api = _api()
+    dev, ops = _gpu_ops(inputs)
+    f = ref["fwd"]
+    o32, lse32 = _f32(f["o"]), _f32(f["lse"])
+    d = api.attn_delta(shape, mode, o=o32, do=dev["do"], do_c=ops["do_c"], q_c=ops["q_c"], k_c=ops["k_c"],
+                       v_c=ops["v_c"], lse=lse32)
+    torch.cuda.synchronize()
+    want = ref[mode]["delta"]
+    tol = U.delta_tolerance(shp, ref["ops"], f["lse"], mode, o=f["o"], do=ref["do"])
+    U.compare("delta", d, want, radius=tol + 1e-30, rel=0.0)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("name", list(SMALL))
+def test_bwd_parity(name, mode):
+    w, inputs, shape, shp, ref = _case(name)
+    _log(f"[bwd] {name} {mode}")
+    api = _api()
+    _, ops = _gpu_ops(inputs)
+    r = ref[mode]
+    g = api.attn_bwd(shape, ops, _f32(ref["fwd"]["lse"]), _f32(r["delta"]), probe=True)
+    torch.cuda.synchronize()
+    b = r["bwd"]
+    for n in ("dq", "dk", "dv"):
+        s = U.compare(n, g[n], b[n], radius=b["r_" + n])
+        _log(f"   {s}")
+    # the probe's pre-cast row sums follow the oracle's within the FP32 budget
+    U.compare("rowsum", g["rowsum"], b["rowsum"], radius=2 * A.TAU * b["rowabs"] + 1e-30, rel=0.0)
+    U.compare("rowabs", g["rowabs"], b["rowabs"], radius=2 * A.TAU * b["rowabs"] + 1e-30, rel=0.0)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_chain_matched_rowsums_and_parity(name):
+    """The benchmarked chain (fwd -> matched delta -> bwd) entirely on the GPU."""
+    w, inputs, shape, shp, ref = _case(name)
+    _log(f"[chain matched] {name}")
+    api = _api()
+    _, ops = _gpu_ops(inputs)
+    g = api.fwd_delta_bwd(shape, ops, "matched", probe=True)
+    torch.cuda.synchronize()
+    f, r = ref["fwd"], ref["matched"]
+    U.compare("O", g["o"], f["o"], radius=f["r_o"])
+    for n in ("dq", "dk", "dv"):
+        U.compare(n, g[n], r["bwd"][n], radius=r["bwd"]["r_" + n])
+    rs, ra = U.to64(g["rowsum"]), U.to64(g["rowabs"])
+    assert np.all(np.abs(rs) <= U.ROWSUM_TOL * ra), float(np.max(np.abs(rs) / np.maximum(ra, 1e-300)))
+
+
+@pytest.mark.parametrize("mode", ["stale", "do_matched"])
+@pytest.mark.parametrize("name", ["gqa_ragged", "mla"])
+def test_chain_saved_output_modes(name, mode):
+    """Chain with delta from the kernel's own O: the oracle bound carries O's deviation into delta."""
+    w, inputs, shape, shp, ref = _case(name)
+    _log(f"[chain {mode}] {name}")
+    api = _api()
+    dev, ops = _gpu_ops(inputs)
+    g = api.fwd_delta_bwd(shape, ops, mode, do=dev["do"])
+    torch.cuda.synchronize()
+    f = ref["fwd"]
+    o_tol = U.REL_TOL * float(np.sqrt(np.mean(f["o"] ** 2)))
+    x = ref["do"] if mode == "stale" else ref["ops"]["do_c"]
+    derr = A.delta_error_bound(mode, x, o_tol, f["r_o"]) + U.delta_tolerance(shp, ref["ops"], f["lse"], mode,
+                                                                             o=f["o"], do=ref["do"])
+    U.compare("delta", g["delta"], ref[mode]["delta"], radius=derr, rel=0.0)
+    b = A.backward(ref["ops"], shp, f["lse"], ref[mode]["delta"], radius=True, delta_err=derr)
+    for n in ("dq", "dk", "dv"):
+        U.compare(n, g[n], b[n], radius=b["r_" + n])
+
+
+# ---------------------------------------------------------------------------
+# metamorphic and determinism checks (GPU only)
+# ---------------------------------------------------------------------------
+
+def test_power_of_two_scaling_is_exact():
+    w = SMALL["gqa_ragged"]
+    inputs = W.generate(w)
+    api = _api()
+    shape = api.AttnShape(w.batch, w.heads_q, w.heads_kv, w.seqlen, w.d_qk, w.d_v, w.causal)
+    _, ops = _gpu_ops(inputs)
+    scaled = dict(inputs, v=(inputs["v"].float() * 2).bfloat16(), do=(inputs["do"].float() * 4).bfloat16())
+    _, ops2 = _gpu_ops(scaled)
+    g1 = api.fwd_delta_bwd(shape, ops, "matched")
+    g2 = api.fwd_delta_bwd(shape, ops2, "matched")
+    torch.cuda.synchronize()
+    assert torch.equal(g1["o"] * 2, g2["o"]) and torch.equal(g1["lse"], g2["lse"])
+    assert torch.equal(g1["delta"] * 8, g2["delta"])
+    assert torch.equal(g1["dk"] * 8, g2["dk"]) and torch.equal(g1["dv"] * 4, g2["dv"])
+    # dQ sums key tiles with atomics in no fixed order
+    U.compare("dq", g2["dq"], U.to64(g1["dq"]) * 8, rel=1e-5)
+
+
+def test_run_to_run_determinism():
+    w = SMALL["gqa_gain"]
+    inputs = W.generate(w)
+    api = _api()
+    shape = api.AttnShape(w.batch, w.heads_q, w.heads_kv, w.seqlen, w.d_qk, w.d_v, w.causal)
+    _, ops = _gpu_ops(inputs)
+    a = api.fwd_delta_bwd(shape, ops, "matched")
+    b = api.fwd_delta_bwd(shape, ops, "matched")
+    torch.cuda.synchronize()
+    for n in ("o", "lse", "delta", "dk", "dv"):
+        assert torch.equal(a[n], b[n]), n
+    U.compare("dq", b["dq"], U.to64(a["dq"]), rel=1e-5)
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("L", [1, 33, 128, 129])
+def test_short_and_ragged_lengths(L):
+    w = W.small("short", batch=1, heads_q=2, heads_kv=1, seqlen=L, d_qk=64, d_v=64, causal=True, kind="iid",
+                seed=30 + L)
+    inputs = W.generate(w)
+    api = _api()
+    shape = api.AttnShape(w.batch, w.heads_q, w.heads_kv, L, w.d_qk, w.d_v, True)
+    shp = U.oracle_shape(w, shape.sigma)
+    ref = U.run_oracle(inputs, shp, modes=("matched",))
+    _, ops = _gpu_ops(inputs)
+    g = api.fwd_delta_bwd(shape, ops, "matched", probe=True)
+    torch.cuda.synchronize()
+    U.compare("O", g["o"], ref["fwd"]["o"], radius=ref["fwd"]["r_o"])
+    b = ref["matched"]["bwd"]
+    for n in ("dq", "dk", "dv"):
+        U.compare(n, g[n], b[n], radius=b["r_" + n])
+    # causal row 0 sees only key 0: O_0 equals the decoded V row exactly
+    v0 = ref["ops"]["v_s"][0, 0, 0]
+    assert np.array_equal(U.to64(g["o"])[0, 0, 0], v0)
+
+
+def test_zero_length_is_a_noop():
+    api = _api()
+    shape = api.AttnShape(1, 1, 1, 0, 64, 64, True)
+    z = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    s = torch.zeros(4, dtype=torch.float32, device="cuda")
+    op = api.Fp8Operand(z, s)
+    o = torch.full((4,), 7.0, device="cuda")
+    api.attn_fwd(shape, op, op, op, o=o, lse=o)
+    torch.cuda.synchronize()
+    assert torch.all(o == 7.0)
+
+
+def test_zero_inputs_and_zero_queries():
+    """All-zero operands (clamped scales) and Q = 0 (uniform attention: O is a running mean of V_hat)."""
+    w = W.small("zeros", batch=1, heads_q=1, heads_kv=1, seqlen=200, d_qk=128, d_v=128, causal=True,
+                kind="iid", seed=40)
+    inputs = W.generate(w)
+    inputs["q"] = torch.zeros_like(inputs["q"])
+    api = _api()
+    shape = api.AttnShape(1, 1, 1, 200, 128, 128, True)
+    _, ops = _gpu_ops(inputs)
+    g = api.fwd_delta_bwd(shape, ops, "matched", probe=True)
+    torch.cuda.synchronize()
+    vs = A.decode_operands({"v_s": A.quantize_sequence(U.to64(inputs["v"]), "e4m3")}, 200)["v_s"][0, 0]
+    mean = np.cumsum(vs, axis=0) / np.arange(1, 201)[:, None]
+    U.compare("O", g["o"][0, 0], mean, rel=1e-6)
+    assert np.allclose(U.to64(g["lse"])[0, 0], np.log(np.arange(1, 201)), atol=1e-5)
+    zero = {n: torch.zeros_like(t) for n, t in inputs.items()}
+    _, zops = _gpu_ops(zero)
+    gz = api.fwd_delta_bwd(shape, zops, "matched", probe=True)
+    torch.cuda.synchronize()
+    for n in ("o", "delta", "dq", "dk", "dv"):
+        assert torch.count_nonzero(gz[n]) == 0, n
