@@ -38,7 +38,10 @@ struct BwdSmem {
   int dsksc[kBQ * 4];
   float lse[kBQ];
   float del[kBQ];
+  float pabs[kBQ];                 // probe: per-query sum_j |P dP^| over the workgroup's keys
   float tr[4 * kBQ * kTP];
+  uint8_t kt[DQK * KROW];          // K^<s> rows (channels) over the workgroup's 128 keys
+  float ktsc[DQK * 4];
 };
 
 template <int DQK, int DV, bool CAUSAL, bool PROBE>
@@ -52,10 +55,8 @@ __global__ __launch_bounds__(256) void bwd_kernel(
     double* __restrict__ psum, double* __restrict__ pabs, int Hq, int Hkv, int L, int Lp, float sigma) {
   constexpr int KS = DQK / 64, VS = DV / 64, KB = DQK / 32, VB = DV / 32;
   constexpr int NKT = DQK / 32, NVT = DV / 32;
-  constexpr int NQT_W = (NKT + 3) / 4;            // dQ channel tiles per wave (upper bound)
   using SM = BwdSmem<DQK, DV>;
   __shared__ __attribute__((aligned(16))) SM sm;
-  __shared__ __attribute__((aligned(16))) float tra[PROBE ? 4 * kBQ * kTP : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -86,23 +87,13 @@ __global__ __launch_bounds__(256) void bwd_kernel(
       vsc[s] = e8m0(vps[2 * s + h]);
     }
   }
-  // K^<s> rows (channels) of this wave's dQ tiles over the workgroup's 128 keys
-  v8i kt[NQT_W][2];
-  int ktsc[NQT_W][2];
-#pragma unroll
-  for (int m = 0; m < NQT_W; ++m) {
-    const int ct = w + 4 * m;
-    if (ct < NKT) {
-      const int ch = 32 * ct + R;
-      const uint8_t* p = kst + (khead * DQK + ch) * Lp + k0;
-      const float* ps = ksts + (khead * DQK + ch) * LB + k0 / kBlock;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        kt[m][s] = cat(*reinterpret_cast<const v4i*>(p + 64 * s + 16 * h), *reinterpret_cast<const v4i*>(p + 64 * s + 32 + 16 * h));
-        ktsc[m][s] = e8m0(ps[2 * s + h]);
-      }
-    }
+  // K^<s> rows (channels) over the workgroup's 128 keys, staged once in LDS for dQ
+  for (int i = tid; i < DQK * 8; i += 256) {
+    const int r = i / 8, c = (i % 8) * 16;
+    *reinterpret_cast<v4i*>(sm.kt + r * SM::KROW + c) = *reinterpret_cast<const v4i*>(kst + (khead * DQK + r) * Lp + k0 + c);
   }
+  for (int i = tid; i < DQK; i += 256)
+    *reinterpret_cast<v4f*>(sm.ktsc + 4 * i) = *reinterpret_cast<const v4f*>(ksts + (khead * DQK + i) * LB + k0 / kBlock);
 
   v16f dkacc[NKT], dvacc[NVT];
 #pragma unroll
@@ -143,6 +134,7 @@ __global__ __launch_bounds__(256) void bwd_kernel(
         const int q = q0 + tid;
         sm.lse[tid] = q < L ? lse[qhead * L + q] * kLog2e : INFINITY;
         sm.del[tid] = q < L ? delta[qhead * L + q] : 0.f;
+        if constexpr (PROBE) sm.pabs[tid] = 0.f;
       }
       __syncthreads();
 
@@ -244,14 +236,13 @@ __global__ __launch_bounds__(256) void bwd_kernel(
 #pragma unroll
           for (int v = 0; v < 16; ++v) tw[(32 * tq + 16 * h + v) * kTP + R] = dp[tq][v];
         if constexpr (PROBE) {
-          float* ta = tra + w * kBQ * kTP;
+          // |P dP^| = |dS + P delta|, summed over this wave's keys into the step's per-query slots
 #pragma unroll
           for (int tq = 0; tq < 2; ++tq)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-              // |P dP^| recovered from P and dS: P dP^ = dS + P delta
               const int qq = 32 * tq + 16 * h + v;
-              ta[qq * kTP + R] = fabsf(dp[tq][v] + s[tq][v] * sm.del[qq]);
+              atomicAdd(&sm.pabs[qq], fabsf(dp[tq][v] + s[tq][v] * sm.del[qq]));
             }
         }
       }
@@ -280,47 +271,39 @@ __global__ __launch_bounds__(256) void bwd_kernel(
           *reinterpret_cast<v4i*>(sm.dsk + qq * SM::KROW + 32 * w + 16 * h) = cw;
           if (h == 0) sm.dsksc[qq * 4 + w] = k + 127;
           if constexpr (PROBE) {
-            float rs = 0.f, ra = 0.f;
-            const float* ta = tra + w * kBQ * kTP;
+            float rs = 0.f;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              rs += x[v];
-              ra += ta[qq * kTP + 16 * h + v];
-            }
+            for (int v = 0; v < 16; ++v) rs += x[v];
             rs = pair_sum(rs);
-            ra = pair_sum(ra);
             const int q = q0 + qq;
-            if (h == 0 && q < L) {
-              atomicAdd(psum + qhead * L + q, (double)rs);
-              atomicAdd(pabs + qhead * L + q, (double)ra);
-            }
+            if (h == 0 && q < L) atomicAdd(psum + qhead * L + q, (double)rs);
+            if (w == 0 && h == 0 && q < L) atomicAdd(pabs + qhead * L + q, (double)sm.pabs[qq]);
           }
         }
       }
       __syncthreads();
-      // ---- dQ^T = K^<s>^T dS^<k>^T over the workgroup's 128 keys, added to dq
+      // ---- dQ = dS^<k> K^<s> over the workgroup's 128 keys, added to dq.  The output
+      // tile has 32 consecutive channels across the lanes of each register, so each
+      // atomic instruction covers two 128-byte row segments; rows past L add zero to
+      // row L-1 so that no lane branches around the matrix instructions.
+      for (int t = w; t < 2 * NKT; t += 4) {
+        const int ct = t >> 1, tq = t & 1;
+        const int qq = 32 * tq + R;
+        v16f acc = v16f{};
 #pragma unroll
-      for (int m = 0; m < NQT_W; ++m) {
-        const int ct = w + 4 * m;
-        if (ct >= NKT) break;
+        for (int st = 0; st < 2; ++st) {
+          const uint8_t* pa = sm.dsk + qq * SM::KROW + 64 * st;
+          const uint8_t* pb = sm.kt + (32 * ct + R) * SM::KROW + 64 * st;
+          v8i a = cat(lds_read16(pa + 16 * h), lds_read16(pa + 32 + 16 * h));
+          v8i bb = cat(lds_read16(pb + 16 * h), lds_read16(pb + 32 + 16 * h));
+          acc = mfma<E5M2, E4M3>(a, bb, acc, sm.dsksc[qq * 4 + 2 * st + h],
+                                 e8m0(sm.ktsc[(32 * ct + R) * 4 + 2 * st + h]));
+        }
 #pragma unroll
-        for (int tq = 0; tq < 2; ++tq) {
-          const int qq = 32 * tq + R;
-          v16f acc = v16f{};
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            const uint8_t* p = sm.dsk + qq * SM::KROW + 64 * st;
-            v8i bop = cat(lds_read16(p + 16 * h), lds_read16(p + 32 + 16 * h));
-            acc = mfma<E4M3, E5M2>(kt[m][st], bop, acc, ktsc[m][st], sm.dsksc[qq * 4 + 2 * st + h]);
-          }
-          const int q = q0 + qq;
-          if (q < L) {
-            float* dst = dq + (qhead * L + q) * DQK + 32 * ct + 4 * h;
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) atomicAdd(dst + 8 * a + e, sigma * acc[4 * a + e]);
-          }
+        for (int v = 0; v < 16; ++v) {
+          const int q = q0 + 32 * tq + 8 * (v >> 2) + 4 * h + (v & 3);
+          const int qc = q < L ? q : L - 1;
+          atomicAdd(dq + (qhead * L + qc) * DQK + 32 * ct + R, q < L ? sigma * acc[v] : 0.f);
         }
       }
     }

@@ -11,7 +11,13 @@ import torch
 from oracle import attention as A
 from fp8_attention_amd.workloads import Workload
 
-REL_TOL = 2e-3          # max-abs error <= REL_TOL * RMS(oracle tensor) (+ cast-ambiguity radius)
+REL_TOL = 2e-3          # max-abs error <= REL_TOL * RMS(oracle tensor) (+ allowance)
+# Norm-wise bar.  The FP8 matrix instruction's own accumulation error and the
+# cast flips it triggers (both legitimate, both inside the elementwise
+# allowance) put ||gpu - oracle|| / ||oracle|| at 1e-3 .. 3.6e-3 on the test
+# workloads; 5e-3 keeps a bar that any systematic error (a wrong scale, index
+# or mask) exceeds by orders of magnitude.
+NORM_TOL = 5e-3
 ROWSUM_TOL = 1e-5       # |sum_j dS_ij| <= ROWSUM_TOL * sum_j |P_ij dP_ij| under Delta-Matching
 
 
@@ -32,7 +38,11 @@ def select_group(inputs: dict, w: Workload, b: int, g: int) -> dict:
 
 
 def run_oracle(inputs: dict, shp: A.Shape, modes=("matched",), rows=None, radius=True) -> dict:
-    """Oracle forward + every requested delta mode + backward, with radii."""
+    """Oracle forward + every requested delta mode + backward, with radii and bounds.
+
+    The backward is evaluated with the oracle's own LSE and delta (float32
+    rounding only), which is what the kernel-isolated tests feed the GPU.
+    """
     q, k, v, do = (to64(inputs[n]) for n in ("q", "k", "v", "do"))
     qops = A.quantize_operands(q, k, v, do)
     ops = A.decode_operands(qops, shp.seqlen)
@@ -44,8 +54,15 @@ def run_oracle(inputs: dict, shp: A.Shape, modes=("matched",), rows=None, radius
     return out
 
 
-def compare(name: str, gpu, ref: np.ndarray, radius=None, rel: float = REL_TOL, mask=None) -> dict:
-    """Assert |gpu - ref| <= rel * RMS(ref) + radius elementwise over finite ref entries."""
+def compare(name: str, gpu, ref: np.ndarray, allow=None, rel: float = REL_TOL, mask=None,
+            norm_rel=None) -> dict:
+    """Assert |gpu - ref| <= rel * RMS(ref) + allow elementwise over finite ref entries.
+
+    ``allow`` is the oracle's bound of how far a correct kernel result may sit
+    from the exact value (ambiguous-cast radius plus the matrix cores'
+    accumulation error).  With ``norm_rel`` also assert the norm-wise bar
+    ||gpu - ref||_2 <= norm_rel * ||ref||_2 over the same entries.
+    """
     g = to64(gpu) if isinstance(gpu, torch.Tensor) else np.asarray(gpu, dtype=np.float64)
     ok = np.isfinite(ref)
     if mask is not None:
@@ -54,29 +71,17 @@ def compare(name: str, gpu, ref: np.ndarray, radius=None, rel: float = REL_TOL, 
     rms = float(np.sqrt(np.mean(ref[ok] ** 2)))
     err = np.abs(g - ref)
     base = rel * rms
-    tol = base + (0.0 if radius is None else np.where(np.isfinite(radius), radius, 0.0))
+    tol = base + (0.0 if allow is None else np.where(np.isfinite(allow), allow, 0.0))
     bad = ok & ~(err <= tol)
+    nrel = float(np.sqrt(np.sum(err[ok] ** 2)) / max(np.sqrt(np.sum(ref[ok] ** 2)), 1e-300))
     stats = {"name": name, "rms": rms, "max_err_over_rms": float(err[ok].max() / max(rms, 1e-300)),
-             "n": int(ok.sum()), "n_used_radius": int((ok & (err > base)).sum()), "n_bad": int(bad.sum())}
+             "norm_rel_err": nrel, "n": int(ok.sum()), "n_beyond_rel_rms": int((ok & (err > base)).sum()),
+             "n_bad": int(bad.sum())}
     if bad.any():
         idx = np.argwhere(bad)[:5]
         detail = [(tuple(int(i) for i in ix), float(g[tuple(ix)]), float(ref[tuple(ix)]),
                    float(tol if np.isscalar(tol) else tol[tuple(ix)])) for ix in idx]
         raise AssertionError(f"{name}: {stats} first bad (index, gpu, oracle, tol): {detail}")
+    if norm_rel is not None:
+        assert nrel <= norm_rel, f"{name}: norm-wise relative error {nrel:.3e} > {norm_rel:.1e} ({stats})"
     return stats
-
-
-def delta_tolerance(shp: A.Shape, ops: dict, lse, mode: str, o=None, do=None) -> np.ndarray:
-    """Per-row bound of FP32 rounding in delta: TAU * sum of |terms| of its defining sum."""
-    if mode == "matched":
-        G = shp.group
-        tol = np.zeros((shp.batch, shp.heads_q, shp.seqlen))
-        for b in range(shp.batch):
-            for h in range(shp.heads_q):
-                P = A.probs_rows(ops["q_c"][b, h], ops["k_c"][b, h // G], lse[b, h], shp.sigma, shp.causal, 0,
-                                 shp.seqlen)
-                dP = ops["do_c"][b, h] @ ops["v_c"][b, h // G].T
-                tol[b, h] = A.TAU * np.abs(P * dP).sum(axis=1)
-        return tol
-    x = do if mode == "stale" else ops["do_c"]
-    return A.TAU * np.einsum("...k,...k->...", np.abs(x), np.abs(o))

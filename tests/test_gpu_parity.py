@@ -1,11 +1,13 @@
 """GPU parity of libdm against the CPU oracle (run with ``-m gpu`` on an MI355X).
 
-Bar (per tensor): FP8 codes and scales bit-exact; O, dQ, dK, dV within
-2e-3 x RMS(oracle) elementwise, plus the first-order radius of in-kernel casts
-whose exact input lies within FP32 rounding of a rounding or scale boundary
-(both casts are correct there); LSE and delta within their FP32 rounding
-budget; under Delta-Matching |sum_j dS_ij| <= 1e-5 sum_j |P_ij dP_ij| on the
-kernel's own pre-cast dS.
+Bar (per tensor): FP8 codes and scales bit-exact.  O, dQ, dK, dV: norm-wise
+||gpu - oracle|| <= 2e-3 ||oracle||, and elementwise |gpu - oracle| <=
+2e-3 RMS(oracle) + allowance, where the allowance is the oracle's bound of
+(a) the FP8 matrix cores' own accumulation error on that output and (b) the
+first-order radius of in-kernel casts whose exact input lies within the
+kernel's error budget of a rounding or scale boundary (both casts are correct
+there).  LSE and delta within their error bounds.  Under Delta-Matching
+|sum_j dS_ij| <= 1e-5 sum_j |P_ij dP_ij| on the kernel's own pre-cast dS.
 """
 import functools
 import sys
@@ -142,9 +144,8 @@ def test_fwd_parity(name):
     o, lse = api.attn_fwd(shape, ops["q_c"], ops["k_c"], ops["v_s"])
     torch.cuda.synchronize()
     f = ref["fwd"]
-    s = U.compare("O", o, f["o"], radius=f["r_o"])
-    lse_tol = A.TAU * (np.abs(f["lse"]) + 1.0)
-    U.compare("LSE", lse, f["lse"], radius=lse_tol, rel=0.0)
+    s = U.compare("O", o, f["o"], allow=f["r_o"] + f["b_o"], norm_rel=U.NORM_TOL)
+    U.compare("LSE", lse, f["lse"], allow=f["b_lse"], rel=0.0)
     _log(f"   {s} flagged casts {f['n_flag']} blocks {f['n_block_flag']}")
 
 
@@ -161,8 +162,8 @@ def test_delta_parity(name, mode):
                        v_c=ops["v_c"], lse=lse32)
     torch.cuda.synchronize()
     want = ref[mode]["delta"]
-    tol = U.delta_tolerance(shp, ref["ops"], f["lse"], mode, o=f["o"], do=ref["do"])
-    U.compare("delta", d, want, radius=tol + 1e-30, rel=0.0)
+    tol = A.delta_bound(ref["ops"], shp, mode, o=f["o"], do=ref["do"], lse=f["lse"])
+    U.compare("delta", d, want, allow=tol + 1e-30, rel=0.0)
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -177,11 +178,11 @@ def test_bwd_parity(name, mode):
     torch.cuda.synchronize()
     b = r["bwd"]
     for n in ("dq", "dk", "dv"):
-        s = U.compare(n, g[n], b[n], radius=b["r_" + n])
+        s = U.compare(n, g[n], b[n], allow=b["r_" + n] + b["b_" + n], norm_rel=U.NORM_TOL)
         _log(f"   {s}")
-    # the probe's pre-cast row sums follow the oracle's within the FP32 budget
-    U.compare("rowsum", g["rowsum"], b["rowsum"], radius=2 * A.TAU * b["rowabs"] + 1e-30, rel=0.0)
-    U.compare("rowabs", g["rowabs"], b["rowabs"], radius=2 * A.TAU * b["rowabs"] + 1e-30, rel=0.0)
+    # the probe's pre-cast row sums follow the oracle's within the kernel's error bound
+    U.compare("rowsum", g["rowsum"], b["rowsum"], allow=b["b_rowsum"] + 1e-30, rel=0.0)
+    U.compare("rowabs", g["rowabs"], b["rowabs"], allow=b["b_rowsum"] + 1e-30, rel=0.0)
 
 
 @pytest.mark.parametrize("name", list(SMALL))
@@ -194,9 +195,12 @@ def test_chain_matched_rowsums_and_parity(name):
     g = api.fwd_delta_bwd(shape, ops, "matched", probe=True)
     torch.cuda.synchronize()
     f, r = ref["fwd"], ref["matched"]
-    U.compare("O", g["o"], f["o"], radius=f["r_o"])
+    U.compare("O", g["o"], f["o"], allow=f["r_o"] + f["b_o"], norm_rel=U.NORM_TOL)
+    derr = A.delta_bound(ref["ops"], shp, "matched", lse=f["lse"], lse_err=f["b_lse"])
+    U.compare("delta", g["delta"], r["delta"], allow=derr, rel=0.0)
+    b = A.backward(ref["ops"], shp, f["lse"], r["delta"], radius=True, delta_err=derr, lse_err=f["b_lse"])
     for n in ("dq", "dk", "dv"):
-        U.compare(n, g[n], r["bwd"][n], radius=r["bwd"]["r_" + n])
+        _log("   ", U.compare(n, g[n], b[n], allow=b["r_" + n] + b["b_" + n], norm_rel=U.NORM_TOL))
     rs, ra = U.to64(g["rowsum"]), U.to64(g["rowabs"])
     assert np.all(np.abs(rs) <= U.ROWSUM_TOL * ra), float(np.max(np.abs(rs) / np.maximum(ra, 1e-300)))
 
@@ -212,14 +216,12 @@ def test_chain_saved_output_modes(name, mode):
     g = api.fwd_delta_bwd(shape, ops, mode, do=dev["do"])
     torch.cuda.synchronize()
     f = ref["fwd"]
-    o_tol = U.REL_TOL * float(np.sqrt(np.mean(f["o"] ** 2)))
-    x = ref["do"] if mode == "stale" else ref["ops"]["do_c"]
-    derr = A.delta_error_bound(mode, x, o_tol, f["r_o"]) + U.delta_tolerance(shp, ref["ops"], f["lse"], mode,
-                                                                             o=f["o"], do=ref["do"])
-    U.compare("delta", g["delta"], ref[mode]["delta"], radius=derr, rel=0.0)
-    b = A.backward(ref["ops"], shp, f["lse"], ref[mode]["delta"], radius=True, delta_err=derr)
+    o_err = U.REL_TOL * float(np.sqrt(np.mean(f["o"] ** 2))) + f["r_o"] + f["b_o"]
+    derr = A.delta_bound(ref["ops"], shp, mode, o=f["o"], do=ref["do"], o_err=o_err)
+    U.compare("delta", g["delta"], ref[mode]["delta"], allow=derr, rel=0.0)
+    b = A.backward(ref["ops"], shp, f["lse"], ref[mode]["delta"], radius=True, delta_err=derr, lse_err=f["b_lse"])
     for n in ("dq", "dk", "dv"):
-        U.compare(n, g[n], b[n], radius=b["r_" + n])
+        U.compare(n, g[n], b[n], allow=b["r_" + n] + b["b_" + n])
 
 
 # ---------------------------------------------------------------------------
@@ -274,10 +276,13 @@ def test_short_and_ragged_lengths(L):
     _, ops = _gpu_ops(inputs)
     g = api.fwd_delta_bwd(shape, ops, "matched", probe=True)
     torch.cuda.synchronize()
-    U.compare("O", g["o"], ref["fwd"]["o"], radius=ref["fwd"]["r_o"])
-    b = ref["matched"]["bwd"]
+    f = ref["fwd"]
+    U.compare("O", g["o"], f["o"], allow=f["r_o"] + f["b_o"], norm_rel=U.NORM_TOL)
+    derr = A.delta_bound(ref["ops"], shp, "matched", lse=f["lse"], lse_err=f["b_lse"])
+    b = A.backward(ref["ops"], shp, f["lse"], ref["matched"]["delta"], radius=True, delta_err=derr,
+                   lse_err=f["b_lse"])
     for n in ("dq", "dk", "dv"):
-        U.compare(n, g[n], b[n], radius=b["r_" + n])
+        U.compare(n, g[n], b[n], allow=b["r_" + n] + b["b_" + n], norm_rel=U.NORM_TOL)
     # causal row 0 sees only key 0: O_0 equals the decoded V row exactly
     v0 = ref["ops"]["v_s"][0, 0, 0]
     assert np.array_equal(U.to64(g["o"])[0, 0, 0], v0)
@@ -307,8 +312,10 @@ def test_zero_inputs_and_zero_queries():
     g = api.fwd_delta_bwd(shape, ops, "matched", probe=True)
     torch.cuda.synchronize()
     vs = A.decode_operands({"v_s": A.quantize_sequence(U.to64(inputs["v"]), "e4m3")}, 200)["v_s"][0, 0]
-    mean = np.cumsum(vs, axis=0) / np.arange(1, 201)[:, None]
-    U.compare("O", g["o"][0, 0], mean, rel=1e-6)
+    n = np.arange(1, 201)[:, None]
+    mean = np.cumsum(vs, axis=0) / n
+    # every probability is exactly 1 before normalising: only the P V product's accumulation error remains
+    U.compare("O", g["o"][0, 0], mean, rel=1e-6, allow=A.GAMMA * np.cumsum(np.abs(vs), axis=0) / n)
     assert np.allclose(U.to64(g["lse"])[0, 0], np.log(np.arange(1, 201)), atol=1e-5)
     zero = {n: torch.zeros_like(t) for n, t in inputs.items()}
     _, zops = _gpu_ops(zero)
