@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdm.so")
-SOURCES = ["api.hip", "quantize.hip", "attn_fwd.hip", "attn_delta.hip", "attn_bwd.hip"]
+SOURCES = ["api.hip", "quantize.hip", "attn_fwd.hip", "attn_delta.hip", "attn_bwd.hip", "attn_dq.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # keep the compiler away from packed FP32 instructions on this target

@@ -1,43 +1,37 @@
-// Backward of block-scaled FP8 attention on gfx950 matrix cores.
+// dK and dV of block-scaled FP8 attention (key-stationary).
 //
-// Key-stationary: workgroup = 8 waves = 128 keys x 64 queries per step; grid =
-// (key tiles, Hkv, B).  Wave w = (key group kg = w % 4, query half qh = w / 4)
-// owns keys 32kg..32kg+31 and, in each step, queries 32qh..32qh+31 of the
-// step's 64.  A workgroup walks the query heads of its KV group and, for each,
-// the query blocks of 64 that can see its keys.  Per step:
+// Workgroup = 8 waves = 128 keys x 64 queries per step; grid = (key tiles, Hkv,
+// B).  Wave w = (key group kg = w % 4, query half qh = w / 4) owns keys
+// 32kg..32kg+31 and, in each step, queries 32qh..32qh+31 of the step's 64.  A
+// workgroup walks the query heads of its KV group and, for each, the query
+// blocks of 64 that can see its keys.  Per step:
 //   A  S = Q K^T and dP^ = dO V^T for the wave's 32x32 tile (scaled FP8 MFMA;
 //      one key per lane pair, 16 queries per lane); P = exp(S - LSE) and
 //      dS = P (dP^ - delta) in FP32; the 32-query block casts P^<q> (E4M3) and
-//      dS^<q> (E5M2) happen in registers; codes go to LDS for the partner wave
-//      of the other query half, dS (FP32) goes to an LDS transpose buffer;
+//      dS^<q> (E5M2) happen in registers and the codes go to LDS for the
+//      partner wave of the other query half;
 //   B  dV^T += dO^<s>^T P^<q> and dK^T += Q^<s>^T dS^<q> over the 64 queries,
-//      each wave taking half of the channel tiles of its key group; the dS
-//      transpose is read back one query per lane pair and cast along keys
-//      (dS^<k>, E5M2);
-//   C  dQ = dS^<k> K^<s> over the 128 keys, one output tile per wave, added to
-//      dq with coalesced FP32 atomics.
+//      each wave taking half of the channel tiles of its key group.
 // The next step's query-side operands are loaded into registers while the
 // current step computes.  dK and dV accumulate in registers over every query
-// head of the group and are written once.
+// head of the group and are written once (no atomics).  dQ is computed by the
+// query-stationary kernel in attn_dq.hip.
 #include "dm_common.h"
 #include "dm_internal.h"
 
 namespace dm {
 
 constexpr int kBQ = 64;          // queries per step
-constexpr int kTP = 36;          // LDS pitch (floats) of the dS transpose rows
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 
 template <int DQK, int DV>
 struct BwdSmem {
-  static constexpr int QROW = DQK + 16, VROW = DV + 16, TROW = kBQ + 16, KROW = 128 + 16;
+  static constexpr int QROW = DQK + 16, VROW = DV + 16, TROW = kBQ + 16;
   uint8_t q[kBQ * QROW];                 // Q^<c> rows of the step
   uint8_t dO[kBQ * VROW];                // dO^<c> rows
   uint8_t qt[DQK * TROW];                // Q^<s>: channel rows over the step's 64 queries
   uint8_t dOt[DV * TROW];                // dO^<s>
-  uint8_t dsk[kBQ * KROW];               // dS^<k> codes: 64 queries x 128 keys
-  uint8_t kt[DQK * KROW];                // K^<s>: channel rows over the workgroup's 128 keys
   v4i pc[4 * 2 * 64];                    // P^<q> codes per (key group, query half, lane)
   v4i dc[4 * 2 * 64];                    // dS^<q> codes
   int psc[4 * 2 * 64];                   // their E8M0 scales
@@ -46,21 +40,19 @@ struct BwdSmem {
   float dOsc[kBQ * (DV / 32)];
   float qtsc[DQK * 2];
   float dOtsc[DV * 2];
-  float ktsc[DQK * 4];
-  int dsksc[kBQ * 4];
   float lse[kBQ];
   float del[kBQ];
-  float pabs[kBQ];                       // probe: per-query sum_j |P dP^| over the workgroup's keys
-  float tr[4 * kBQ * kTP];               // dS transpose, one 64 x 32 slab per key group
 };
 
-// V^<c> rows of the workgroup's 128 keys, kept in LDS (instead of registers) when
-// the LDS budget allows it (d_qk <= 128), to keep the wave under 256 VGPRs.
-template <int DV, bool ON>
-struct VTile {
-  static constexpr int ROW = DV + 16;
-  uint8_t v[ON ? 128 * ROW : 16];
-  float vsc[ON ? 128 * (DV / 32) : 4];
+// K^<c> and V^<c> rows of the workgroup's 128 keys, read from LDS as the B
+// operands of S and dP^ (keeps the wave well under 256 VGPRs).
+template <int DQK, int DV>
+struct KVTile {
+  static constexpr int KROW = DQK + 16, VROW = DV + 16;
+  uint8_t k[128 * KROW];
+  uint8_t v[128 * VROW];
+  float ksc[128 * (DQK / 32)];
+  float vsc[128 * (DV / 32)];
 };
 
 // Register staging of one step's query-side operands (loaded a step ahead).
@@ -110,7 +102,7 @@ __device__ __forceinline__ void prefetch(Prefetch<DQK, DV>& pf, int tid, int64_t
   }
 }
 
-template <int DQK, int DV, bool PROBE>
+template <int DQK, int DV>
 __device__ __forceinline__ void commit(const Prefetch<DQK, DV>& pf, BwdSmem<DQK, DV>& sm, int tid) {
   using P = Prefetch<DQK, DV>;
   using SM = BwdSmem<DQK, DV>;
@@ -141,27 +133,24 @@ __device__ __forceinline__ void commit(const Prefetch<DQK, DV>& pf, BwdSmem<DQK,
   if (tid < kBQ) {
     sm.lse[tid] = pf.lse;
     sm.del[tid] = pf.del;
-    if constexpr (PROBE) sm.pabs[tid] = 0.f;
   }
 }
 
-template <int DQK, int DV, bool CAUSAL, bool PROBE>
-__global__ __launch_bounds__(kThreads) void bwd_kernel(
+template <int DQK, int DV, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void dkdv_kernel(
     const uint8_t* __restrict__ qc, const float* __restrict__ qcs, const uint8_t* __restrict__ qs,
     const float* __restrict__ qss, const uint8_t* __restrict__ kc, const float* __restrict__ kcs,
-    const uint8_t* __restrict__ kst, const float* __restrict__ ksts, const uint8_t* __restrict__ vc,
-    const float* __restrict__ vcs, const uint8_t* __restrict__ doc, const float* __restrict__ docs,
-    const uint8_t* __restrict__ dos, const float* __restrict__ doss, const float* __restrict__ lse,
-    const float* __restrict__ delta, float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv,
-    double* __restrict__ psum, double* __restrict__ pabs, int Hq, int Hkv, int L, int Lp, float sigma) {
+    const uint8_t* __restrict__ vc, const float* __restrict__ vcs, const uint8_t* __restrict__ doc,
+    const float* __restrict__ docs, const uint8_t* __restrict__ dos, const float* __restrict__ doss,
+    const float* __restrict__ lse, const float* __restrict__ delta, float* __restrict__ dk, float* __restrict__ dv,
+    int Hq, int Hkv, int L, int Lp, float sigma) {
   constexpr int KS = DQK / 64, VS = DV / 64, KB = DQK / 32, VB = DV / 32;
   constexpr int NKT = DQK / 32, NVT = DV / 32;
   constexpr int NKW = NKT / 2, NVW = NVT / 2;     // channel tiles of dK^T / dV^T per wave
   using SM = BwdSmem<DQK, DV>;
-  constexpr bool VLDS = DQK <= 128;
-  using VT = VTile<DV, VLDS>;
+  using KV = KVTile<DQK, DV>;
   __shared__ __attribute__((aligned(16))) SM sm;
-  __shared__ __attribute__((aligned(16))) VT vt;
+  __shared__ __attribute__((aligned(16))) KV kv;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -171,44 +160,20 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
   const int hk = blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv;
   const int key = k0 + 32 * kg + R;                  // this lane's key (column of S tiles)
+  const int kr = 32 * kg + R;                        // its row in the workgroup's K/V tiles
   const int64_t khead = (int64_t)b * Hkv + hk;
-  const int LB = Lp / kBlock;
 
-  // resident key-side operands (B operands of S and dP^)
-  v8i kb[KS], vb[VLDS ? 1 : VS];
-  int ksc[KS], vsc[VLDS ? 1 : VS];
-  {
-    const uint8_t* kp = kc + (khead * Lp + key) * DQK;
-    const float* kps = kcs + (khead * Lp + key) * KB;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      kb[s] = cat(*reinterpret_cast<const v4i*>(kp + 64 * s + 16 * h), *reinterpret_cast<const v4i*>(kp + 64 * s + 32 + 16 * h));
-      ksc[s] = e8m0(kps[2 * s + h]);
-    }
-    if constexpr (!VLDS) {
-      const uint8_t* vp = vc + (khead * Lp + key) * DV;
-      const float* vps = vcs + (khead * Lp + key) * VB;
-#pragma unroll
-      for (int s = 0; s < VS; ++s) {
-        vb[s] = cat(*reinterpret_cast<const v4i*>(vp + 64 * s + 16 * h), *reinterpret_cast<const v4i*>(vp + 64 * s + 32 + 16 * h));
-        vsc[s] = e8m0(vps[2 * s + h]);
-      }
-    }
+  // the workgroup's K^<c> and V^<c> rows, staged once
+  for (int i = tid; i < 128 * DQK / 16; i += kThreads) {
+    const int r = (i * 16) / DQK, c = (i * 16) % DQK;
+    *reinterpret_cast<v4i*>(kv.k + r * KV::KROW + c) = *reinterpret_cast<const v4i*>(kc + (khead * Lp + k0 + r) * DQK + c);
   }
-  if constexpr (VLDS) {
-    for (int i = tid; i < 128 * DV / 16; i += kThreads) {
-      const int r = (i * 16) / DV, c = (i * 16) % DV;
-      *reinterpret_cast<v4i*>(vt.v + r * VT::ROW + c) = *reinterpret_cast<const v4i*>(vc + (khead * Lp + k0 + r) * DV + c);
-    }
-    for (int i = tid; i < 128 * VB; i += kThreads) vt.vsc[i] = vcs[(khead * Lp + k0) * VB + i];
+  for (int i = tid; i < 128 * DV / 16; i += kThreads) {
+    const int r = (i * 16) / DV, c = (i * 16) % DV;
+    *reinterpret_cast<v4i*>(kv.v + r * KV::VROW + c) = *reinterpret_cast<const v4i*>(vc + (khead * Lp + k0 + r) * DV + c);
   }
-  // K^<s> rows (channels) over the workgroup's 128 keys, staged once for dQ
-  for (int i = tid; i < DQK * 8; i += kThreads) {
-    const int r = i / 8, c = (i % 8) * 16;
-    *reinterpret_cast<v4i*>(sm.kt + r * SM::KROW + c) = *reinterpret_cast<const v4i*>(kst + (khead * DQK + r) * Lp + k0 + c);
-  }
-  for (int i = tid; i < DQK; i += kThreads)
-    *reinterpret_cast<v4f*>(sm.ktsc + 4 * i) = *reinterpret_cast<const v4f*>(ksts + (khead * DQK + i) * LB + k0 / kBlock);
+  for (int i = tid; i < 128 * KB; i += kThreads) kv.ksc[i] = kcs[(khead * Lp + k0) * KB + i];
+  for (int i = tid; i < 128 * VB; i += kThreads) kv.vsc[i] = vcs[(khead * Lp + k0) * VB + i];
 
   v16f dkacc[NKW], dvacc[NVW];
 #pragma unroll
@@ -225,13 +190,12 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
   Prefetch<DQK, DV> pf;
   prefetch<DQK, DV>(pf, tid, (int64_t)b * Hq + hk * G, qstart, L, Lp, qc, qcs, qs, qss, doc, docs, dos, doss, lse,
                     delta);
-  commit<DQK, DV, PROBE>(pf, sm, tid);
+  commit<DQK, DV>(pf, sm, tid);
   __syncthreads();
 
   for (int it = 0; it < total; ++it) {
     const int hh = it / nsteps;
     const int q0 = qstart + (it - hh * nsteps) * kBQ;
-    const int64_t qhead = (int64_t)b * Hq + hk * G + hh;
     if (it + 1 < total) {
       const int hn = (it + 1) / nsteps;
       prefetch<DQK, DV>(pf, tid, (int64_t)b * Hq + hk * G + hn, qstart + (it + 1 - hn * nsteps) * kBQ, L, Lp, qc,
@@ -243,21 +207,18 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const uint8_t* p = sm.q + arow * SM::QROW + 64 * ks;
+      const uint8_t* pk = kv.k + kr * KV::KROW + 64 * ks;
       v8i a = cat(lds_read16(p + 16 * h), lds_read16(p + 32 + 16 * h));
-      s = mfma<E4M3, E4M3>(a, kb[ks], s, e8m0(sm.qsc[arow * KB + 2 * ks + h]), ksc[ks]);
+      v8i bk = cat(lds_read16(pk + 16 * h), lds_read16(pk + 32 + 16 * h));
+      s = mfma<E4M3, E4M3>(a, bk, s, e8m0(sm.qsc[arow * KB + 2 * ks + h]), e8m0(kv.ksc[kr * KB + 2 * ks + h]));
     }
 #pragma unroll
     for (int ks = 0; ks < VS; ++ks) {
       const uint8_t* p = sm.dO + arow * SM::VROW + 64 * ks;
+      const uint8_t* pv = kv.v + kr * KV::VROW + 64 * ks;
       v8i a = cat(lds_read16(p + 16 * h), lds_read16(p + 32 + 16 * h));
-      if constexpr (VLDS) {
-        const int kr = 32 * kg + R;
-        const uint8_t* pv = vt.v + kr * VT::ROW + 64 * ks;
-        v8i bv = cat(lds_read16(pv + 16 * h), lds_read16(pv + 32 + 16 * h));
-        dp = mfma<E5M2, E4M3>(a, bv, dp, e8m0(sm.dOsc[arow * VB + 2 * ks + h]), e8m0(vt.vsc[kr * VB + 2 * ks + h]));
-      } else {
-        dp = mfma<E5M2, E4M3>(a, vb[ks], dp, e8m0(sm.dOsc[arow * VB + 2 * ks + h]), vsc[ks]);
-      }
+      v8i bv = cat(lds_read16(pv + 16 * h), lds_read16(pv + 32 + 16 * h));
+      dp = mfma<E5M2, E4M3>(a, bv, dp, e8m0(sm.dOsc[arow * VB + 2 * ks + h]), e8m0(kv.vsc[kr * VB + 2 * ks + h]));
     }
     const bool need_mask = (k0 + 128 > L) || (CAUSAL && q0 < k0 + 128);
     const int qb = 32 * qh + 16 * h;               // first step-query of this lane's 16
@@ -298,14 +259,6 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
       sm.dc[slot] = dw;
       sm.psc[slot] = kp + 127;
       sm.dsc[slot] = kd + 127;
-      float* tw = sm.tr + kg * kBQ * kTP;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) tw[(qb + v) * kTP + R] = dp[v];
-      if constexpr (PROBE) {
-        // |P dP^| = |dS + P delta|, summed over the keys into the step's per-query slots
-#pragma unroll
-        for (int v = 0; v < 16; ++v) atomicAdd(&sm.pabs[qb + v], fabsf(dp[v] + s[v] * sm.del[qb + v]));
-      }
     }
     __syncthreads();
 
@@ -331,70 +284,12 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
         dkacc[m] = mfma<E4M3, E5M2>(a, dsq, dkacc[m], e8m0(sm.qtsc[ch * 2 + h]), dsc);
       }
     }
-    {
-      // dS^<k>: lane pair (query 32qh + R) reads the 32 keys of group kg
-      const int qq = 32 * qh + R;
-      const float* tw = sm.tr + kg * kBQ * kTP + qq * kTP + 16 * h;
-      float x[16];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const v4f t4 = *reinterpret_cast<const v4f*>(tw + 4 * g);
-        x[4 * g] = t4[0]; x[4 * g + 1] = t4[1]; x[4 * g + 2] = t4[2]; x[4 * g + 3] = t4[3];
-      }
-      float am = 0.f;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) am = fmaxf(am, fabsf(x[v]));
-      am = pair_max(am);
-      const int k = scale_exp<E5M2>(am);
-      const float inv = exp2i(-k);
-      v4i cw;
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        cw[g] = (int)pack4<E5M2>(x[4 * g] * inv, x[4 * g + 1] * inv, x[4 * g + 2] * inv, x[4 * g + 3] * inv);
-      *reinterpret_cast<v4i*>(sm.dsk + qq * SM::KROW + 32 * kg + 16 * h) = cw;
-      if (h == 0) sm.dsksc[qq * 4 + kg] = k + 127;
-      if constexpr (PROBE) {
-        float rs = 0.f;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) rs += x[v];
-        rs = pair_sum(rs);
-        // branch-free: every lane adds, pad rows and the second lane of each pair add zero
-        const int q = q0 + qq;
-        const int qcl = q < L ? q : L - 1;
-        const bool own = h == 0 && q < L;
-        atomicAdd(psum + qhead * L + qcl, own ? (double)rs : 0.0);
-        atomicAdd(pabs + qhead * L + qcl, own && kg == 0 ? (double)sm.pabs[qq] : 0.0);
-      }
-    }
     __syncthreads();
-
-    // ---- C: dQ = dS^<k> K^<s> over the workgroup's 128 keys, added to dq.  The output
-    // tile has 32 consecutive channels across the lanes of each register, so each
-    // atomic instruction covers two 128-byte row segments; rows past L add zero to
-    // row L-1 so that no lane branches around the matrix instructions.
-    // The staging buffers are free now: the next step's operands go in first.
-    if (it + 1 < total) commit<DQK, DV, PROBE>(pf, sm, tid);
-    for (int t = w; t < 2 * NKT; t += kWaves) {
-      const int ct = t >> 1, tq = t & 1;
-      const int qq = 32 * tq + R;
-      v16f acc = v16f{};
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const uint8_t* pa = sm.dsk + qq * SM::KROW + 64 * st;
-        const uint8_t* pb = sm.kt + (32 * ct + R) * SM::KROW + 64 * st;
-        v8i a = cat(lds_read16(pa + 16 * h), lds_read16(pa + 32 + 16 * h));
-        v8i bb = cat(lds_read16(pb + 16 * h), lds_read16(pb + 32 + 16 * h));
-        acc = mfma<E5M2, E4M3>(a, bb, acc, sm.dsksc[qq * 4 + 2 * st + h],
-                               e8m0(sm.ktsc[(32 * ct + R) * 4 + 2 * st + h]));
-      }
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int q = q0 + 32 * tq + 8 * (v >> 2) + 4 * h + (v & 3);
-        const int qcl = q < L ? q : L - 1;
-        atomicAdd(dq + (qhead * L + qcl) * DQK + 32 * ct + R, q < L ? sigma * acc[v] : 0.f);
-      }
+    // every read of this step's staging buffers is done: the next step's operands go in
+    if (it + 1 < total) {
+      commit<DQK, DV>(pf, sm, tid);
+      __syncthreads();
     }
-    __syncthreads();
   }
 
   // ---- dK, dV written once per key: wave (kg, qh) holds channel tiles qh, qh+2, ...
@@ -419,6 +314,35 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
   }
 }
 
+template <int DQK, int DV>
+static void launch_dkdv_t(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand vc, Operand doc,
+                          Operand dos, const float* lse, const float* delta, float* dk, float* dv, hipStream_t s) {
+  dim3 grid(d.Lp / 128, d.Hkv, d.B);
+  if (d.causal)
+    hipLaunchKernelGGL((dkdv_kernel<DQK, DV, true>), grid, dim3(kThreads), 0, s, qc.codes, qc.scales, qs.codes,
+                       qs.scales, kc.codes, kc.scales, vc.codes, vc.scales, doc.codes, doc.scales, dos.codes,
+                       dos.scales, lse, delta, dk, dv, d.Hq, d.Hkv, d.L, d.Lp, d.sigma);
+  else
+    hipLaunchKernelGGL((dkdv_kernel<DQK, DV, false>), grid, dim3(kThreads), 0, s, qc.codes, qc.scales, qs.codes,
+                       qs.scales, kc.codes, kc.scales, vc.codes, vc.scales, doc.codes, doc.scales, dos.codes,
+                       dos.scales, lse, delta, dk, dv, d.Hq, d.Hkv, d.L, d.Lp, d.sigma);
+}
+
+hipError_t launch_bwd(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand ks, Operand vc, Operand doc,
+                      Operand dos, const float* lse, const float* delta, float* dq, float* dk, float* dv,
+                      double* ps, double* pa, hipStream_t s) {
+  if (d.dqk == 64 && d.dv == 64) launch_dkdv_t<64, 64>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);
+  else if (d.dqk == 128 && d.dv == 128) launch_dkdv_t<128, 128>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);
+  else if (d.dqk == 192 && d.dv == 128) launch_dkdv_t<192, 128>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);
+  else if (d.dqk == 64 && d.dv == 128) launch_dkdv_t<64, 128>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);
+  else if (d.dqk == 128 && d.dv == 64) launch_dkdv_t<128, 64>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);
+  else if (d.dqk == 192 && d.dv == 64) launch_dkdv_t<192, 64>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);
+  else return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_dq(d, qc, kc, ks, vc, doc, lse, delta, dq, ps, pa, s);
+}
+
 __global__ void fill_zero_kernel(uint64_t* p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
 }
@@ -429,49 +353,6 @@ hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t s) {
   int64_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<uint64_t*>(p), n);
-  return hipGetLastError();
-}
-
-template <int DQK, int DV, bool CAUSAL, bool PROBE>
-static void launch_bwd_t4(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand ks, Operand vc, Operand doc,
-                          Operand dos, const float* lse, const float* delta, float* dq, float* dk, float* dv,
-                          double* ps, double* pa, hipStream_t s) {
-  dim3 grid(d.Lp / 128, d.Hkv, d.B);
-  hipLaunchKernelGGL((bwd_kernel<DQK, DV, CAUSAL, PROBE>), grid, dim3(kThreads), 0, s, qc.codes, qc.scales, qs.codes,
-                     qs.scales, kc.codes, kc.scales, ks.codes, ks.scales, vc.codes, vc.scales, doc.codes, doc.scales,
-                     dos.codes, dos.scales, lse, delta, dq, dk, dv, ps, pa, d.Hq, d.Hkv, d.L, d.Lp, d.sigma);
-}
-
-template <int DQK, int DV>
-static void launch_bwd_t(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand ks, Operand vc, Operand doc,
-                         Operand dos, const float* lse, const float* delta, float* dq, float* dk, float* dv,
-                         double* ps, double* pa, hipStream_t s) {
-  const bool probe = ps != nullptr;
-  if (d.causal) {
-    if (probe) launch_bwd_t4<DQK, DV, true, true>(d, qc, qs, kc, ks, vc, doc, dos, lse, delta, dq, dk, dv, ps, pa, s);
-    else launch_bwd_t4<DQK, DV, true, false>(d, qc, qs, kc, ks, vc, doc, dos, lse, delta, dq, dk, dv, ps, pa, s);
-  } else {
-    if (probe) launch_bwd_t4<DQK, DV, false, true>(d, qc, qs, kc, ks, vc, doc, dos, lse, delta, dq, dk, dv, ps, pa, s);
-    else launch_bwd_t4<DQK, DV, false, false>(d, qc, qs, kc, ks, vc, doc, dos, lse, delta, dq, dk, dv, ps, pa, s);
-  }
-}
-
-hipError_t launch_bwd(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand ks, Operand vc, Operand doc,
-                      Operand dos, const float* lse, const float* delta, float* dq, float* dk, float* dv,
-                      double* ps, double* pa, hipStream_t s) {
-  hipError_t e = launch_fill_zero(dq, (int64_t)d.B * d.Hq * d.L * d.dqk * 4, s);
-  if (e != hipSuccess) return e;
-  if (ps) {
-    if ((e = launch_fill_zero(ps, (int64_t)d.B * d.Hq * d.L * 8, s)) != hipSuccess) return e;
-    if ((e = launch_fill_zero(pa, (int64_t)d.B * d.Hq * d.L * 8, s)) != hipSuccess) return e;
-  }
-  if (d.dqk == 64 && d.dv == 64) launch_bwd_t<64, 64>(d, qc, qs, kc, ks, vc, doc, dos, lse, delta, dq, dk, dv, ps, pa, s);
-  else if (d.dqk == 128 && d.dv == 128) launch_bwd_t<128, 128>(d, qc, qs, kc, ks, vc, doc, dos, lse, delta, dq, dk, dv, ps, pa, s);
-  else if (d.dqk == 192 && d.dv == 128) launch_bwd_t<192, 128>(d, qc, qs, kc, ks, vc, doc, dos, lse, delta, dq, dk, dv, ps, pa, s);
-  else if (d.dqk == 64 && d.dv == 128) launch_bwd_t<64, 128>(d, qc, qs, kc, ks, vc, doc, dos, lse, delta, dq, dk, dv, ps, pa, s);
-  else if (d.dqk == 128 && d.dv == 64) launch_bwd_t<128, 64>(d, qc, qs, kc, ks, vc, doc, dos, lse, delta, dq, dk, dv, ps, pa, s);
-  else if (d.dqk == 192 && d.dv == 64) launch_bwd_t<192, 64>(d, qc, qs, kc, ks, vc, doc, dos, lse, delta, dq, dk, dv, ps, pa, s);
-  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -85,7 +85,7 @@ hipError_t launch_delta_rows(const AttnDims& d, int mode, const float* o, const 
 // matched
 // ---------------------------------------------------------------------------
 template <int DQK, int DV, bool CAUSAL>
-__global__ __launch_bounds__(256) void delta_matched_kernel(
+__global__ __launch_bounds__(256, 2) void delta_matched_kernel(
     const uint8_t* __restrict__ qc, const float* __restrict__ qcs, const uint8_t* __restrict__ kc,
     const float* __restrict__ kcs, const uint8_t* __restrict__ vc, const float* __restrict__ vcs,
     const uint8_t* __restrict__ doc, const float* __restrict__ docs, const float* __restrict__ lse,
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) void delta_matched_kernel(
   }
   const float c2 = sigma * kLog2e;
   const float l2 = (qi < L) ? lse[qhead * L + qi] * kLog2e : 0.f;
-  float acc = 0.f;
+  double acc = 0.0;                              // FP32 per chunk, FP64 across chunks
   const int nchunks = CAUSAL ? (qt + 1) : nqt;
   const int krow_a = pair_row(R);
   for (int c = 0; c < nchunks; ++c) {
@@ -154,6 +154,7 @@ __global__ __launch_bounds__(256) void delta_matched_kernel(
     __syncthreads();
     if (CAUSAL && k0 > q0 + 32 * w + 31) continue;
     const bool need_mask = (k0 + kChunk > L) || (CAUSAL && k0 + kChunk - 1 > q0 + 32 * w);
+    float cacc = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int krow = 32 * t + krow_a;
@@ -170,20 +171,23 @@ __global__ __launch_bounds__(256) void delta_matched_kernel(
         v8i a = cat(lds_read16(p + 16 * h), lds_read16(p + 32 + 16 * h));
         dp = mfma<E4M3, E5M2>(a, db[ks], dp, e8m0(sVs[krow * VB + 2 * ks + h]), dsc[ks]);
       }
+      if (need_mask) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int kk = k0 + 32 * t + 16 * h + v;
+          if (kk >= L || (CAUSAL && kk > qi)) s[v] = -INFINITY;
+        }
+      }
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        float x = s[v];
-        if (need_mask) {
-          const int kk = k0 + 32 * t + 16 * h + v;
-          if (kk >= L || (CAUSAL && kk > qi)) x = -INFINITY;
-        }
-        const float p = __builtin_amdgcn_exp2f(fmaf(x, c2, -l2));
-        acc = fmaf(p, dp[v], acc);
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[v], c2, -l2));
+        cacc = fmaf(p, dp[v], cacc);
       }
     }
+    acc += (double)cacc;
   }
-  acc = pair_sum(acc);
-  if (qi < L && h == 0) delta[qhead * L + qi] = acc;
+  acc = pair_sum_d(acc);
+  if (qi < L && h == 0) delta[qhead * L + qi] = (float)acc;
 }
 
 template <int DQK, int DV>

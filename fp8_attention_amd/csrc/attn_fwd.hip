@@ -20,7 +20,7 @@
 namespace dm {
 
 template <int DQK, int DV, bool CAUSAL>
-__global__ __launch_bounds__(256) void fwd_kernel(const uint8_t* __restrict__ qc, const float* __restrict__ qcs,
+__global__ __launch_bounds__(256, 2) void fwd_kernel(const uint8_t* __restrict__ qc, const float* __restrict__ qcs,
                                                   const uint8_t* __restrict__ kc, const float* __restrict__ kcs,
                                                   const uint8_t* __restrict__ vs, const float* __restrict__ vss,
                                                   float* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv,
@@ -63,7 +63,8 @@ __global__ __launch_bounds__(256) void fwd_kernel(const uint8_t* __restrict__ qc
   }
 
   const float c2 = sigma * kLog2e;
-  float mu = -INFINITY, l = 0.f;
+  float mu = -INFINITY;
+  double l = 0.0;                                // FP32 per chunk, FP64 across chunks
   v16f oacc[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) oacc[ct] = v16f{};
@@ -115,39 +116,47 @@ __global__ __launch_bounds__(256) void fwd_kernel(const uint8_t* __restrict__ qc
           if (kk >= L || (CAUSAL && kk > qi)) s[t][v] = -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    // block maxima of the raw scores; exp2 is monotone, so the block amax of P' is
+    // exp2 of the block max, computed by the same instructions as that element
+    float bm[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t) {
+      float m = s[t][0];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[t][v]);
-    mx = pair_max(mx);
+      for (int v = 1; v < 16; ++v) m = fmaxf(m, s[t][v]);
+      bm[t] = pair_max(m);
+    }
+    const float mx = fmaxf(fmaxf(bm[0], bm[1]), fmaxf(bm[2], bm[3]));
     const float mu_new = fmaxf(mu, mx);
     const float m2 = (mu_new == -INFINITY) ? 0.f : mu_new * c2;
     const float alpha = __builtin_amdgcn_exp2f(mu * c2 - m2);
     mu = mu_new;
-    l *= alpha;
+    l *= (double)alpha;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) oacc[ct] *= alpha;
+      for (int ct = 0; ct < NCT; ++ct) oacc[ct] *= alpha;
+    }
 
     v8i pb[2];
     int psc[2] = {0, 0};
+    float lc = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      float am = 0.f;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[t][v], c2, -m2));
-        s[t][v] = p;
-        l += p;
-        am = fmaxf(am, p);
-      }
-      am = pair_max(am);
+      const float am = __builtin_amdgcn_exp2f(fmaf(bm[t], c2, -m2));
       const int k = scale_exp<E4M3>(am);
       const float inv = exp2i(-k);
+      float ls = 0.f;
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        pb[t >> 1][4 * (t & 1) + g] =
-            (int)pack4<E4M3>(s[t][4 * g] * inv, s[t][4 * g + 1] * inv, s[t][4 * g + 2] * inv, s[t][4 * g + 3] * inv);
+      for (int g = 0; g < 4; ++g) {
+        float p4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p4[e] = __builtin_amdgcn_exp2f(fmaf(s[t][4 * g + e], c2, -m2));
+          ls += p4[e];
+        }
+        pb[t >> 1][4 * (t & 1) + g] = (int)pack4<E4M3>(p4[0] * inv, p4[1] * inv, p4[2] * inv, p4[3] * inv);
+      }
+      lc += ls;
       if ((t & 1) == h) psc[t >> 1] = k + 127;
     }
 #pragma unroll
@@ -159,11 +168,12 @@ __global__ __launch_bounds__(256) void fwd_kernel(const uint8_t* __restrict__ qc
         v8i a = cat(lds_read16(p + 16 * h), lds_read16(p + 32 + 16 * h));
         oacc[ct] = mfma<E4M3, E4M3>(a, pb[st], oacc[ct], e8m0(sVs[vrow * 4 + 2 * st + h]), psc[st]);
       }
+    l += (double)lc;
   }
 
-  l = pair_sum(l);
+  l = pair_sum_d(l);
   if (qi < L) {
-    const float inv_l = 1.f / l;
+    const float inv_l = (float)(1.0 / l);
     float* orow = o + (qhead * L + qi) * DV;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
@@ -173,7 +183,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(const uint8_t* __restrict__ qc
                  oacc[ct][4 * a + 3] * inv_l};
         *reinterpret_cast<v4f*>(orow + 32 * ct + 8 * a + 4 * h) = r;
       }
-    if (h == 0) lse[qhead * L + qi] = mu * sigma + logf(l);
+    if (h == 0) lse[qhead * L + qi] = (float)((double)mu * sigma + log(l));
   }
 }
 

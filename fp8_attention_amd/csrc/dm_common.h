@@ -75,6 +75,16 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+__device__ __forceinline__ double pair_sum_d(double x) {
+  const uint64_t u = __double_as_longlong(x);
+  const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+  auto rl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  auto rh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  const double a = __longlong_as_double(((uint64_t)rh[0] << 32) | rl[0]);
+  const double b = __longlong_as_double(((uint64_t)rh[1] << 32) | rl[1]);
+  return a + b;
+}
+
 template <int FA, int FB>
 __device__ __forceinline__ v16f mfma(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, sa, 0, sb);

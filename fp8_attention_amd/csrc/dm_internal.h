@@ -31,6 +31,9 @@ hipError_t launch_bwd(const AttnDims& d, Operand q_c, Operand q_s, Operand k_c, 
                       Operand do_c, Operand do_s, const float* lse, const float* delta, float* dq, float* dk,
                       float* dv, double* probe_sum, double* probe_abs, hipStream_t s);
 
+hipError_t launch_dq(const AttnDims& d, Operand qc, Operand kc, Operand ks, Operand vc, Operand doc,
+                     const float* lse, const float* delta, float* dq, double* ps, double* pa, hipStream_t s);
+
 hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t s);
 
 }  // namespace dm
