@@ -75,7 +75,20 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extra", action="store_true", help="also time quantize and the saved-output delta modes")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB three times (for calibrating rocprofv3's "
+                         "FETCH_SIZE / WRITE_SIZE against a known byte count) and exit")
     args = ap.parse_args()
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        a = torch.ones(n, dtype=torch.uint8, device="cuda")
+        c = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            c.copy_(a)
+        torch.cuda.synchronize()
+        _log(f"[bench] copied {n} bytes three times")
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested); the path has no multi-GPU form.",
               file=sys.stderr)

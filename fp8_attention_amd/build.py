@@ -19,9 +19,14 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
+# Attention kernels: scores are finite or -inf by construction, so max
+# reductions need no NaN canonicalisation (this lets them map onto v_max3_f32).
+EXTRA = {src: ["-fno-honor-nans"] for src in ("attn_fwd.hip", "attn_delta.hip", "attn_bwd.hip", "attn_dq.hip")}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

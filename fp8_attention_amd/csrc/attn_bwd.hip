@@ -247,12 +247,12 @@ __global__ __launch_bounds__(kThreads) void dkdv_kernel(
       am = pair_max(am);
       dm = pair_max(dm);
       const int kp = scale_exp<E4M3>(am), kd = scale_exp<E5M2>(dm);
-      const float ip = exp2i(-kp), id = exp2i(-kd);
+      const float sp = exp2i(kp), sd = exp2i(kd);
       v4i pw, dw;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        pw[g] = (int)pack4<E4M3>(s[4 * g] * ip, s[4 * g + 1] * ip, s[4 * g + 2] * ip, s[4 * g + 3] * ip);
-        dw[g] = (int)pack4<E5M2>(dp[4 * g] * id, dp[4 * g + 1] * id, dp[4 * g + 2] * id, dp[4 * g + 3] * id);
+        pw[g] = (int)pack4s<E4M3>(s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3], sp);
+        dw[g] = (int)pack4s<E5M2>(dp[4 * g], dp[4 * g + 1], dp[4 * g + 2], dp[4 * g + 3], sd);
       }
       const int slot = (kg * 2 + qh) * 64 + lane;
       sm.pc[slot] = pw;

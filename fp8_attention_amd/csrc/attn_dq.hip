@@ -143,11 +143,10 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
       }
       am = pair_max(am);
       const int k = scale_exp<E5M2>(am);
-      const float inv = exp2i(-k);
+      const float sc = exp2i(k);
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        dsb[t >> 1][4 * (t & 1) + g] =
-            (int)pack4<E5M2>(s[4 * g] * inv, s[4 * g + 1] * inv, s[4 * g + 2] * inv, s[4 * g + 3] * inv);
+        dsb[t >> 1][4 * (t & 1) + g] = (int)pack4s<E5M2>(s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3], sc);
       if ((t & 1) == h) dssc[t >> 1] = k + 127;
     }
 #pragma unroll

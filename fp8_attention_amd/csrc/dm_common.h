@@ -64,6 +64,25 @@ __device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d) {
   return w;
 }
 
+typedef short v2s __attribute__((ext_vector_type(2)));
+
+// Same packing with the block scale applied by the convert itself:
+// v_cvt_scalef32_pk_{fp8,bf8}_f32 rounds x / scale to nearest even (checked
+// bit for bit against the format definitions), which saves the multiply.
+template <int F>
+__device__ __forceinline__ uint32_t pack4s(float a, float b, float c, float d, float scale) {
+  // both halves are written below; starting from a's bits spares a register copy
+  v2s w = __builtin_bit_cast(v2s, a);
+  if constexpr (F == E4M3) {
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a, b, scale, false);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, scale, true);
+  } else {
+    w = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(w, a, b, scale, false);
+    w = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(w, c, d, scale, true);
+  }
+  return __builtin_bit_cast(uint32_t, w);
+}
+
 // The other lane of a (l, l^32) pair: returns {x_lo_lane, x_hi_lane} ordered
 // so that max/sum of the two gives the pair reduction on both lanes.
 __device__ __forceinline__ float pair_max(float x) {
@@ -90,6 +109,14 @@ __device__ __forceinline__ v16f mfma(const v8i& a, const v8i& b, const v16f& c, 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, sa, 0, sb);
 }
 
+// Maximum of the 16 accumulator values of one lane (max3 chain).
+__device__ __forceinline__ float max16(const v16f& x) {
+  float m = fmaxf(fmaxf(x[0], x[1]), x[2]);
+#pragma unroll
+  for (int v = 3; v < 15; v += 2) m = fmaxf(fmaxf(m, x[v]), x[v + 1]);
+  return fmaxf(m, x[15]);
+}
+
 // E8M0 byte of a float32 power-of-two scale (its biased exponent).
 __device__ __forceinline__ int e8m0(float s) { return (int)(__float_as_uint(s) >> 23); }
 
@@ -108,5 +135,30 @@ __device__ __forceinline__ v8i cat(const v4i& lo, const v4i& hi) {
 }
 
 __device__ __forceinline__ v4i lds_read16(const uint8_t* p) { return *reinterpret_cast<const v4i*>(p); }
+
+// ---------------------------------------------------------------------------
+// LDS tiles filled by direct global->LDS loads (global_load_lds_dwordx4: lane l
+// of one instruction writes 16 bytes at LDS base + 16*l, from its own global
+// address), with the 16-byte chunks of each row XOR-swizzled so that the
+// matrix-operand reads (16 bytes per lane, rows in pair_row order or natural
+// order) hit distinct banks for both 8- and 16-lane bank groups.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int swz_f(int r) {          // 3-bit row signature, from row bits 0..4
+  return ((r >> 1) & 1) | (((r ^ (r >> 2)) & 1) << 1) | (((r ^ (r >> 3) ^ (r >> 4)) & 1) << 2);
+}
+// position of logical 16-byte chunk c in a row of NCH chunks (an involution)
+template <int NCH>
+__device__ __forceinline__ int swz(int c, int f) {
+  if constexpr (NCH % 8 == 0) return c ^ f;
+  else if constexpr (NCH == 4) return c ^ (f & 3);
+  else return c < 8 ? (c ^ f) : (8 + ((c - 8) ^ (f & 3)));   // 12 chunks
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void dma16(const void* g, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);
+}
+// wait for this wave's outstanding global loads (including direct-to-LDS ones)
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 }  // namespace dm

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void quantize_cols_kernel(const T* __restrict_
     for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
     am = quad_max(am);
     const int k = scale_exp<F>(am);
-    const float inv = exp2i(-k);
+    const float inv = exp2i(-k);                   // exact; keeps subnormal inputs exact too
     uint32_t w0 = pack4<F>(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
     uint32_t w1 = pack4<F>(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
     if (live) {
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const T* __restrict_
     am = fmaxf(am, fmaxf(fmaxf(fabsf(q[0]), fabsf(q[1])), fmaxf(fabsf(q[2]), fabsf(q[3]))));
   }
   const int k = scale_exp<F>(am);
-  const float inv = exp2i(-k);
+  const float inv = exp2i(-k);                     // exact; keeps subnormal inputs exact too
   v4i o0, o1;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
