@@ -55,7 +55,6 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_kernel(
   constexpr int KS = DQK / 64;      // 64-channel steps of QK^T
   constexpr int NCT = DV / 32;      // 32-channel tiles of O^T
   constexpr int KB = DQK / 32;      // channel blocks per K row
-  constexpr int NCHK = DQK / 16;    // 16-byte chunks per K row
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::BYTES];
 
   const int tid = threadIdx.x;
@@ -82,12 +81,12 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_kernel(
   for (int i = 0; i < C::NKW; ++i) {
     const int p = (w + kFwdWaves * i) * 1024 + 16 * lane;
     const int r = p / DQK, slot = (p % DQK) / 16;
-    koff[i] = r * DQK + 16 * swz<NCHK>(slot, swz_f(r));
+    koff[i] = r * DQK + 16 * tile_slot<DQK>(r, slot);
   }
 #pragma unroll
   for (int i = 0; i < C::NVW; ++i) {
     const int r = 8 * (w + kFwdWaves * i) + (lane >> 3);   // 8 channel rows of 128 B per load
-    voff[i] = (lane >> 3) * Lp + 16 * swz<8>(lane & 7, swz_f(r));
+    voff[i] = (lane >> 3) * Lp + 16 * tile_slot<kChunk>(r, lane & 7);
   }
   auto issue_k = [&](int cc, int buf) {       // K^<c> chunk cc (codes + scales) -> K buffer buf
     const uint8_t* src = Kc + (int64_t)cc * kChunk * DQK;
@@ -129,17 +128,16 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_kernel(
 
   // LDS read offsets of this lane: K rows in pair_row order, V rows natural
   const int kr = pair_row(R);
-  const int fk = swz_f(kr), fv = swz_f(R);
   int kro[KS][2], vro[2][2];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    kro[ks][0] = kr * DQK + 16 * swz<NCHK>(4 * ks + h, fk);
-    kro[ks][1] = kr * DQK + 16 * swz<NCHK>(4 * ks + 2 + h, fk);
+    kro[ks][0] = kr * DQK + 16 * tile_slot<DQK>(kr, 4 * ks + h);
+    kro[ks][1] = kr * DQK + 16 * tile_slot<DQK>(kr, 4 * ks + 2 + h);
   }
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
-    vro[st][0] = R * kChunk + 16 * swz<8>(4 * st + h, fv);
-    vro[st][1] = R * kChunk + 16 * swz<8>(4 * st + 2 + h, fv);
+    vro[st][0] = R * kChunk + 16 * tile_slot<kChunk>(R, 4 * st + h);
+    vro[st][1] = R * kChunk + 16 * tile_slot<kChunk>(R, 4 * st + 2 + h);
   }
 
   const float c2 = sigma * kLog2e;

@@ -139,19 +139,25 @@ __device__ __forceinline__ v4i lds_read16(const uint8_t* p) { return *reinterpre
 // ---------------------------------------------------------------------------
 // LDS tiles filled by direct global->LDS loads (global_load_lds_dwordx4: lane l
 // of one instruction writes 16 bytes at LDS base + 16*l, from its own global
-// address), with the 16-byte chunks of each row XOR-swizzled so that the
-// matrix-operand reads (16 bytes per lane, rows in pair_row order or natural
-// order) hit distinct banks for both 8- and 16-lane bank groups.
+// address).  The 16-byte chunks of each tile row are XOR-permuted by a function
+// of the row index so that the matrix-operand reads (16 bytes per lane, rows in
+// pair_row order or natural order) run at full LDS rate.  The permutations were
+// chosen by timing ds_read_b128 on gfx950 for these access patterns; the plain
+// layout of a 128-byte-row tile runs several times slower.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int swz_f(int r) {          // 3-bit row signature, from row bits 0..4
-  return ((r >> 1) & 1) | (((r ^ (r >> 2)) & 1) << 1) | (((r ^ (r >> 3) ^ (r >> 4)) & 1) << 2);
-}
-// position of logical 16-byte chunk c in a row of NCH chunks (an involution)
-template <int NCH>
-__device__ __forceinline__ int swz(int c, int f) {
-  if constexpr (NCH % 8 == 0) return c ^ f;
-  else if constexpr (NCH == 4) return c ^ (f & 3);
-  else return c < 8 ? (c ^ f) : (8 + ((c - 8) ^ (f & 3)));   // 12 chunks
+// Slot (16-byte position within the row) of logical chunk c of tile row `row`,
+// for rows of RB bytes.  Each map is an involution on the row's chunks.
+template <int RB>
+__device__ __forceinline__ int tile_slot(int row, int c) {
+  if constexpr (RB == 128) {
+    return c ^ ((row >> 1) & 7);
+  } else if constexpr (RB == 64) {
+    return c ^ ((row >> 2) & 3);
+  } else {
+    static_assert(RB == 192, "tile rows of 64, 128 or 192 bytes");
+    const int f = ((row >> 2) & 1) | (((row ^ (row >> 3)) & 1) << 1);
+    return c < 8 ? (c ^ f) : 8 + ((c - 8) ^ f);
+  }
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
