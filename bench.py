@@ -31,14 +31,25 @@ def _log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def bwd_flops(w) -> float:
-    pairs = w.seqlen * w.seqlen / (2.0 if w.causal else 1.0)
-    return 2.0 * (3 * w.d_qk + 2 * w.d_v) * pairs * w.batch * w.heads_q
+def _pairs(w) -> float:
+    return w.seqlen * w.seqlen / (2.0 if w.causal else 1.0) * w.batch * w.heads_q
 
 
+# Matmul FLOPs each kernel executes (its own recomputation of S and dP^ included):
+#   forward  S, P'V            2 (d_qk + d_v) per pair
+#   delta    S, dP^            2 (d_qk + d_v)
+#   dK/dV    S, dP^, dV, dK    2 (2 d_qk + 2 d_v)
+#   dQ       S, dP^, dQ        2 (2 d_qk + d_v)
 def fwd_flops(w) -> float:
-    pairs = w.seqlen * w.seqlen / (2.0 if w.causal else 1.0)
-    return 2.0 * (w.d_qk + w.d_v) * pairs * w.batch * w.heads_q
+    return 2.0 * (w.d_qk + w.d_v) * _pairs(w)
+
+
+def dkdv_flops(w) -> float:
+    return 2.0 * (2 * w.d_qk + 2 * w.d_v) * _pairs(w)
+
+
+def dq_flops(w) -> float:
+    return 2.0 * (2 * w.d_qk + w.d_v) * _pairs(w)
 
 
 def cpu_baseline(w, inputs, rows: int) -> dict:
@@ -124,15 +135,18 @@ def main():
                        lse=lse, out=delta)
         if ev is not None:
             ev[2].record()
-        api.attn_bwd(shape, ops, lse, delta, dq=dq, dk=dk, dv=dv)
+        api.attn_bwd_dkdv(shape, ops, lse, delta, dk=dk, dv=dv)
         if ev is not None:
             ev[3].record()
+        api.attn_bwd_dq(shape, ops, lse, delta, dq=dq)
+        if ev is not None:
+            ev[4].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     # timed region: exactly K steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -142,12 +156,15 @@ def main():
     ms_step = 1e3 * elapsed / args.steps
     k_fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     k_del = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    k_bwd = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    k_dkdv = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    k_dq = float(np.mean([e[3].elapsed_time(e[4]) for e in evs]))
     flops = w.matmul_flops()
     value = flops / (ms_step * 1e-3) / 1e12
-    _log(f"[bench] ms/step {ms_step:.3f} (fwd {k_fwd:.3f}, matched delta {k_del:.3f}, bwd {k_bwd:.3f}) "
+    _log(f"[bench] ms/step {ms_step:.3f} (fwd {k_fwd:.3f}, matched delta {k_del:.3f}, dkdv {k_dkdv:.3f}, "
+         f"dq {k_dq:.3f}) "
          f"-> {value:.1f} TFLOP/s = {100 * value / PEAK_FP8_TFLOPS:.1f}% of FP8 peak")
-    kern = {"fwd": (k_fwd, fwd_flops(w)), "delta_matched": (k_del, fwd_flops(w)), "bwd": (k_bwd, bwd_flops(w))}
+    kern = {"fwd": (k_fwd, fwd_flops(w)), "delta_matched": (k_del, fwd_flops(w)),
+            "bwd_dkdv": (k_dkdv, dkdv_flops(w)), "bwd_dq": (k_dq, dq_flops(w))}
     dom = max(kern, key=lambda n: kern[n][0])
     ach = kern[dom][1] / (kern[dom][0] * 1e-3) / 1e12
     extra = {n: {"ms": t, "tflops_algorithmic": f / (t * 1e-3) / 1e12} for n, (t, f) in kern.items()}

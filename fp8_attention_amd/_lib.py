@@ -19,7 +19,7 @@ DM_DELTA_STALE, DM_DELTA_DO_MATCHED, DM_DELTA_MATCHED = 0, 1, 2
 
 # every symbol include/dm_attn.h declares
 EXPORTS = ("dm_padded_len", "dm_status_string", "dm_quantize_blockfp8", "dm_attn_fwd", "dm_attn_delta",
-           "dm_attn_bwd")
+           "dm_attn_bwd", "dm_attn_bwd_dkdv", "dm_attn_bwd_dq")
 
 
 class Operand(ctypes.Structure):
@@ -64,6 +64,10 @@ def load() -> ctypes.CDLL:
     lib.dm_attn_delta.restype = i32
     lib.dm_attn_bwd.argtypes = [sp] + [Operand] * 7 + [vp] * 7 + [vp]
     lib.dm_attn_bwd.restype = i32
+    lib.dm_attn_bwd_dkdv.argtypes = [sp] + [Operand] * 6 + [vp] * 4 + [vp]
+    lib.dm_attn_bwd_dkdv.restype = i32
+    lib.dm_attn_bwd_dq.argtypes = [sp] + [Operand] * 5 + [vp] * 5 + [vp]
+    lib.dm_attn_bwd_dq.restype = i32
     _lib = lib
     return lib
 

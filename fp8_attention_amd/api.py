@@ -185,6 +185,45 @@ def attn_bwd(shape: AttnShape, ops: dict, lse: torch.Tensor, delta: torch.Tensor
     return out
 
 
+def attn_bwd_dkdv(shape: AttnShape, ops: dict, lse: torch.Tensor, delta: torch.Tensor,
+                  dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None) -> dict:
+    """dm_attn_bwd_dkdv -> {"dk","dv"} float32 (the key-stationary half of dm_attn_bwd)."""
+    dev = lse.device
+    B, Hkv, L = shape.batch, shape.heads_kv, shape.seqlen
+    if dk is None:
+        dk = torch.empty((B, Hkv, L, shape.d_qk), dtype=torch.float32, device=dev)
+    if dv is None:
+        dv = torch.empty((B, Hkv, L, shape.d_v), dtype=torch.float32, device=dev)
+    cs = shape.c()
+    st = _lib.load().dm_attn_bwd_dkdv(ctypes.byref(cs), ops["q_c"].c(), ops["q_s"].c(), ops["k_c"].c(),
+                                      ops["v_c"].c(), ops["do_c"].c(), ops["do_s"].c(), lse.data_ptr(),
+                                      delta.data_ptr(), dk.data_ptr(), dv.data_ptr(), _stream(lse))
+    _lib.check(st, "dm_attn_bwd_dkdv")
+    return {"dk": dk, "dv": dv}
+
+
+def attn_bwd_dq(shape: AttnShape, ops: dict, lse: torch.Tensor, delta: torch.Tensor, probe: bool = False,
+                dq: Optional[torch.Tensor] = None) -> dict:
+    """dm_attn_bwd_dq -> {"dq"} float32 (+ "rowsum","rowabs" probes): the query-stationary half."""
+    dev = lse.device
+    B, Hq, L = shape.batch, shape.heads_q, shape.seqlen
+    if dq is None:
+        dq = torch.empty((B, Hq, L, shape.d_qk), dtype=torch.float32, device=dev)
+    ps = pa = None
+    if probe:
+        ps = torch.empty((B, Hq, L), dtype=torch.float64, device=dev)
+        pa = torch.empty((B, Hq, L), dtype=torch.float64, device=dev)
+    cs = shape.c()
+    st = _lib.load().dm_attn_bwd_dq(ctypes.byref(cs), ops["q_c"].c(), ops["k_c"].c(), ops["k_s"].c(),
+                                    ops["v_c"].c(), ops["do_c"].c(), lse.data_ptr(), delta.data_ptr(),
+                                    dq.data_ptr(), _ptr(ps), _ptr(pa), _stream(lse))
+    _lib.check(st, "dm_attn_bwd_dq")
+    out = {"dq": dq}
+    if probe:
+        out["rowsum"], out["rowabs"] = ps, pa
+    return out
+
+
 def fwd_delta_bwd(shape: AttnShape, ops: dict, mode: str = "matched", do: Optional[torch.Tensor] = None,
                   probe: bool = False) -> dict:
     """One pass of the whole path on already-quantized operands: forward, delta, backward."""

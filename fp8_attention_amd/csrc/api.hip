@@ -140,4 +140,34 @@ dm_status dm_attn_bwd(const dm_attn_shape* shape, dm_fp8_operand q_c, dm_fp8_ope
                                    op(do_s), lse, delta, dq, dk, dv, probe_rowsum_ds, probe_rowsum_abs_pdp, stream));
 }
 
+dm_status dm_attn_bwd_dkdv(const dm_attn_shape* shape, dm_fp8_operand q_c, dm_fp8_operand q_s, dm_fp8_operand k_c,
+                           dm_fp8_operand v_c, dm_fp8_operand do_c, dm_fp8_operand do_s, const float* lse,
+                           const float* delta, float* dk, float* dv, hipStream_t stream) {
+  dm_status st = check_shape(shape);
+  if (st != DM_OK) return st;
+  const dm_fp8_operand ops[6] = {q_c, q_s, k_c, v_c, do_c, do_s};
+  for (const auto& x : ops)
+    if ((st = check_operand(x)) != DM_OK) return st;
+  if ((st = check_ptrs({lse, delta, dk, dv})) != DM_OK) return st;
+  if (shape->seqlen == 0) return DM_OK;
+  return hip_status(dm::launch_dkdv(dims_of(shape), op(q_c), op(q_s), op(k_c), op(v_c), op(do_c), op(do_s), lse,
+                                    delta, dk, dv, stream));
+}
+
+dm_status dm_attn_bwd_dq(const dm_attn_shape* shape, dm_fp8_operand q_c, dm_fp8_operand k_c, dm_fp8_operand k_s,
+                         dm_fp8_operand v_c, dm_fp8_operand do_c, const float* lse, const float* delta, float* dq,
+                         double* probe_rowsum_ds, double* probe_rowsum_abs_pdp, hipStream_t stream) {
+  dm_status st = check_shape(shape);
+  if (st != DM_OK) return st;
+  const dm_fp8_operand ops[5] = {q_c, k_c, k_s, v_c, do_c};
+  for (const auto& x : ops)
+    if ((st = check_operand(x)) != DM_OK) return st;
+  if ((st = check_ptrs({lse, delta, dq})) != DM_OK) return st;
+  if ((probe_rowsum_ds == nullptr) != (probe_rowsum_abs_pdp == nullptr)) return DM_ERR_NULL;
+  if (probe_rowsum_ds && (st = check_ptrs({probe_rowsum_ds, probe_rowsum_abs_pdp})) != DM_OK) return st;
+  if (shape->seqlen == 0) return DM_OK;
+  return hip_status(dm::launch_dq(dims_of(shape), op(q_c), op(k_c), op(k_s), op(v_c), op(do_c), lse, delta, dq,
+                                  probe_rowsum_ds, probe_rowsum_abs_pdp, stream));
+}
+
 }  // extern "C"

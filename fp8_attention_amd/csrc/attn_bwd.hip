@@ -1,315 +1,341 @@
 // dK and dV of block-scaled FP8 attention (key-stationary).
 //
-// Workgroup = 8 waves = 128 keys x 64 queries per step; grid = (key tiles, Hkv,
-// B).  Wave w = (key group kg = w % 4, query half qh = w / 4) owns keys
-// 32kg..32kg+31 and, in each step, queries 32qh..32qh+31 of the step's 64.  A
-// workgroup walks the query heads of its KV group and, for each, the query
-// blocks of 64 that can see its keys.  Per step:
-//   A  S = Q K^T and dP^ = dO V^T for the wave's 32x32 tile (scaled FP8 MFMA;
-//      one key per lane pair, 16 queries per lane); P = exp(S - LSE) and
-//      dS = P (dP^ - delta) in FP32; the 32-query block casts P^<q> (E4M3) and
-//      dS^<q> (E5M2) happen in registers and the codes go to LDS for the
-//      partner wave of the other query half;
-//   B  dV^T += dO^<s>^T P^<q> and dK^T += Q^<s>^T dS^<q> over the 64 queries,
-//      each wave taking half of the channel tiles of its key group.
-// The next step's query-side operands are loaded into registers while the
-// current step computes.  dK and dV accumulate in registers over every query
-// head of the group and are written once (no atomics).  dQ is computed by the
-// query-stationary kernel in attn_dq.hip.
+// Workgroup = NW waves, wave w owning keys k0+32w .. k0+32w+31 and every channel;
+// grid = (Hkv, B, key tiles), key tiles slowest so the long causal tiles start
+// first.  The workgroup walks the query heads of its KV group and, for each, the
+// 64-query steps that can see its keys.  Per step and wave:
+//   S^T = Q K^T and dP^T = dO V^T for two 32-query tiles (scaled FP8 MFMA; one key
+//   per lane pair, 16 queries per lane); P = exp(S - LSE), dS = P (dP^ - delta)
+//   in FP32; the 32-query block casts P^<q> (E4M3) and dS^<q> (E5M2) happen in
+//   registers, and the two tiles' codes side by side are exactly the B operands
+//   of dV^T += dO^<s>^T P^<q> and dK^T += Q^<s>^T dS^<q> (64 queries per product),
+//   so nothing is exchanged between waves.
+// K^<c>/V^<c> of the workgroup's keys sit in LDS for the whole kernel; the
+// query-side tiles of step i+1 (Q^<c>, dO^<c> rows, Q^<s>, dO^<s> channel rows,
+// their scales) arrive in a second LDS buffer by direct global->LDS loads issued
+// during step i, with LSE and delta through registers; one barrier per step.  dK
+// and dV accumulate in registers over every query head of the group and are
+// written once (no atomics).  dQ is computed by the query-stationary kernel in
+// attn_dq.hip.
 #include "dm_common.h"
 #include "dm_internal.h"
 
 namespace dm {
 
 constexpr int kBQ = 64;          // queries per step
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
 
 template <int DQK, int DV>
-struct BwdSmem {
-  static constexpr int QROW = DQK + 16, VROW = DV + 16, TROW = kBQ + 16;
-  uint8_t q[kBQ * QROW];                 // Q^<c> rows of the step
-  uint8_t dO[kBQ * VROW];                // dO^<c> rows
-  uint8_t qt[DQK * TROW];                // Q^<s>: channel rows over the step's 64 queries
-  uint8_t dOt[DV * TROW];                // dO^<s>
-  v4i pc[4 * 2 * 64];                    // P^<q> codes per (key group, query half, lane)
-  v4i dc[4 * 2 * 64];                    // dS^<q> codes
-  int psc[4 * 2 * 64];                   // their E8M0 scales
-  int dsc[4 * 2 * 64];
-  float qsc[kBQ * (DQK / 32)];
-  float dOsc[kBQ * (DV / 32)];
-  float qtsc[DQK * 2];
-  float dOtsc[DV * 2];
-  float lse[kBQ];
-  float del[kBQ];
+struct DkdvCfg {
+  static constexpr int NW = 4;                           // waves (32 keys each), one per SIMD
+  static constexpr int NT = 64 * NW;
+  static constexpr int KT = 32 * NW;                     // keys per workgroup
+  static constexpr int KB = DQK / 32, VB = DV / 32;
+  static constexpr int pad1k(int x) { return (x + 1023) / 1024 * 1024; }
+  // resident K/V tile
+  static constexpr int K_OFF = 0, V_OFF = KT * DQK, KS_OFF = V_OFF + KT * DV, VS_OFF = KS_OFF + KT * KB * 4;
+  static constexpr int KV_BYTES = VS_OFF + KT * VB * 4;
+  // one step's query-side stage (regions padded to whole 1 KB direct loads)
+  static constexpr int QC = 0;                                   // Q^<c> rows [64][DQK], swizzled
+  static constexpr int DOC = QC + pad1k(kBQ * DQK);             // dO^<c> rows [64][DV]
+  static constexpr int QS = DOC + pad1k(kBQ * DV);              // Q^<s> channel rows [DQK][64]
+  static constexpr int DOS = QS + pad1k(DQK * kBQ);             // dO^<s> [DV][64]
+  static constexpr int QCS = DOS + pad1k(DV * kBQ);             // Q^<c> scales [64][KB], query lane order
+  static constexpr int DOCS = QCS + pad1k(kBQ * KB * 4);        // dO^<c> scales [64][VB], lane order
+  static constexpr int NDMA = (DOCS + pad1k(kBQ * VB * 4)) / 1024;   // direct loads per step
+  static constexpr int QSS = NDMA * 1024;                        // Q^<s> scales [DQK][2]   (register path)
+  static constexpr int DOSS = QSS + DQK * 2 * 4;                 // dO^<s> scales [DV][2]
+  static constexpr int LSE = DOSS + DV * 2 * 4;                  // LSE * log2(e) [64]
+  static constexpr int DEL = LSE + kBQ * 4;                      // delta [64]
+  static constexpr int STAGE = pad1k(DEL + kBQ * 4);
+  static constexpr int NSMALL = DQK * 2 + DV * 2 + 2 * kBQ;      // floats through registers per step
+  static constexpr int NSR = (NSMALL + NT - 1) / NT;
+  static constexpr int NDW = (NDMA + NW - 1) / NW;               // direct loads per wave
+  static constexpr int BYTES = KV_BYTES + 2 * STAGE;
+  static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
-
-// K^<c> and V^<c> rows of the workgroup's 128 keys, read from LDS as the B
-// operands of S and dP^ (keeps the wave well under 256 VGPRs).
-template <int DQK, int DV>
-struct KVTile {
-  static constexpr int KROW = DQK + 16, VROW = DV + 16;
-  uint8_t k[128 * KROW];
-  uint8_t v[128 * VROW];
-  float ksc[128 * (DQK / 32)];
-  float vsc[128 * (DV / 32)];
-};
-
-// Register staging of one step's query-side operands (loaded a step ahead).
-template <int DQK, int DV>
-struct Prefetch {
-  static constexpr int NQ = (kBQ * DQK / 16 + kThreads - 1) / kThreads;   // 16-byte pieces per thread
-  static constexpr int NV = (kBQ * DV / 16 + kThreads - 1) / kThreads;
-  v4i q[NQ], qt[NQ], dO[NV], dOt[NV];
-  float qsc, dOsc, qtsc, dOtsc, lse, del;
-};
-
-template <int DQK, int DV>
-__device__ __forceinline__ void prefetch(Prefetch<DQK, DV>& pf, int tid, int64_t qhead, int q0, int L, int Lp,
-                                         const uint8_t* qc, const float* qcs, const uint8_t* qs, const float* qss,
-                                         const uint8_t* doc, const float* docs, const uint8_t* dos,
-                                         const float* doss, const float* lse, const float* delta) {
-  using P = Prefetch<DQK, DV>;
-  const int LB = Lp / kBlock;
-#pragma unroll
-  for (int j = 0; j < P::NQ; ++j) {
-    const int i = tid + j * kThreads;
-    if (i < kBQ * DQK / 16) {
-      const int r = (i * 16) / DQK, c = (i * 16) % DQK;
-      pf.q[j] = *reinterpret_cast<const v4i*>(qc + (qhead * Lp + q0 + r) * DQK + c);
-      const int rt = i / (kBQ / 16), ct = (i % (kBQ / 16)) * 16;
-      pf.qt[j] = *reinterpret_cast<const v4i*>(qs + (qhead * DQK + rt) * Lp + q0 + ct);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < P::NV; ++j) {
-    const int i = tid + j * kThreads;
-    if (i < kBQ * DV / 16) {
-      const int r = (i * 16) / DV, c = (i * 16) % DV;
-      pf.dO[j] = *reinterpret_cast<const v4i*>(doc + (qhead * Lp + q0 + r) * DV + c);
-      const int rt = i / (kBQ / 16), ct = (i % (kBQ / 16)) * 16;
-      pf.dOt[j] = *reinterpret_cast<const v4i*>(dos + (qhead * DV + rt) * Lp + q0 + ct);
-    }
-  }
-  if (tid < kBQ * DQK / 32) pf.qsc = qcs[(qhead * Lp + q0) * (DQK / 32) + tid];
-  if (tid < kBQ * DV / 32) pf.dOsc = docs[(qhead * Lp + q0) * (DV / 32) + tid];
-  if (tid < DQK * 2) pf.qtsc = qss[(qhead * DQK + tid / 2) * LB + q0 / kBlock + (tid & 1)];
-  if (tid < DV * 2) pf.dOtsc = doss[(qhead * DV + tid / 2) * LB + q0 / kBlock + (tid & 1)];
-  if (tid < kBQ) {
-    const int q = q0 + tid;
-    pf.lse = q < L ? lse[qhead * L + q] * kLog2e : INFINITY;
-    pf.del = q < L ? delta[qhead * L + q] : 0.f;
-  }
-}
-
-template <int DQK, int DV>
-__device__ __forceinline__ void commit(const Prefetch<DQK, DV>& pf, BwdSmem<DQK, DV>& sm, int tid) {
-  using P = Prefetch<DQK, DV>;
-  using SM = BwdSmem<DQK, DV>;
-#pragma unroll
-  for (int j = 0; j < P::NQ; ++j) {
-    const int i = tid + j * kThreads;
-    if (i < kBQ * DQK / 16) {
-      const int r = (i * 16) / DQK, c = (i * 16) % DQK;
-      *reinterpret_cast<v4i*>(sm.q + r * SM::QROW + c) = pf.q[j];
-      const int rt = i / (kBQ / 16), ct = (i % (kBQ / 16)) * 16;
-      *reinterpret_cast<v4i*>(sm.qt + rt * SM::TROW + ct) = pf.qt[j];
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < P::NV; ++j) {
-    const int i = tid + j * kThreads;
-    if (i < kBQ * DV / 16) {
-      const int r = (i * 16) / DV, c = (i * 16) % DV;
-      *reinterpret_cast<v4i*>(sm.dO + r * SM::VROW + c) = pf.dO[j];
-      const int rt = i / (kBQ / 16), ct = (i % (kBQ / 16)) * 16;
-      *reinterpret_cast<v4i*>(sm.dOt + rt * SM::TROW + ct) = pf.dOt[j];
-    }
-  }
-  if (tid < kBQ * DQK / 32) sm.qsc[tid] = pf.qsc;
-  if (tid < kBQ * DV / 32) sm.dOsc[tid] = pf.dOsc;
-  if (tid < DQK * 2) sm.qtsc[tid] = pf.qtsc;
-  if (tid < DV * 2) sm.dOtsc[tid] = pf.dOtsc;
-  if (tid < kBQ) {
-    sm.lse[tid] = pf.lse;
-    sm.del[tid] = pf.del;
-  }
-}
 
 template <int DQK, int DV, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void dkdv_kernel(
+__global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
     const uint8_t* __restrict__ qc, const float* __restrict__ qcs, const uint8_t* __restrict__ qs,
     const float* __restrict__ qss, const uint8_t* __restrict__ kc, const float* __restrict__ kcs,
     const uint8_t* __restrict__ vc, const float* __restrict__ vcs, const uint8_t* __restrict__ doc,
     const float* __restrict__ docs, const uint8_t* __restrict__ dos, const float* __restrict__ doss,
     const float* __restrict__ lse, const float* __restrict__ delta, float* __restrict__ dk, float* __restrict__ dv,
     int Hq, int Hkv, int L, int Lp, float sigma) {
-  constexpr int KS = DQK / 64, VS = DV / 64, KB = DQK / 32, VB = DV / 32;
-  constexpr int NKT = DQK / 32, NVT = DV / 32;
-  constexpr int NKW = NKT / 2, NVW = NVT / 2;     // channel tiles of dK^T / dV^T per wave
-  using SM = BwdSmem<DQK, DV>;
-  using KV = KVTile<DQK, DV>;
-  __shared__ __attribute__((aligned(16))) SM sm;
-  __shared__ __attribute__((aligned(16))) KV kv;
+  using C = DkdvCfg<DQK, DV>;
+  constexpr int NW = C::NW, NT = C::NT, KT = C::KT, KB = C::KB, VB = C::VB;
+  constexpr int KS = DQK / 64, VS = DV / 64, NKT = DQK / 32, NVT = DV / 32;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::BYTES];
+  uint8_t* const stage0 = lds + C::KV_BYTES;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
-  const int kg = w & 3, qh = w >> 2;
   const int R = lane & 31, h = lane >> 5;
-  const int k0 = blockIdx.x * 128;
-  const int hk = blockIdx.y, b = blockIdx.z;
+  const int hk = blockIdx.x, b = blockIdx.y;
+  const int k0 = blockIdx.z * KT;
   const int G = Hq / Hkv;
-  const int key = k0 + 32 * kg + R;                  // this lane's key (column of S tiles)
-  const int kr = 32 * kg + R;                        // its row in the workgroup's K/V tiles
+  const int kw0 = k0 + 32 * w;                       // this wave's first key
+  const int key = kw0 + R;                           // this lane's key (column of the S^T tiles)
+  const int LB = Lp / kBlock;
   const int64_t khead = (int64_t)b * Hkv + hk;
 
-  // the workgroup's K^<c> and V^<c> rows, staged once
-  for (int i = tid; i < 128 * DQK / 16; i += kThreads) {
-    const int r = (i * 16) / DQK, c = (i * 16) % DQK;
-    *reinterpret_cast<v4i*>(kv.k + r * KV::KROW + c) = *reinterpret_cast<const v4i*>(kc + (khead * Lp + k0 + r) * DQK + c);
+  // ---- resident K^<c>, V^<c> rows of the workgroup's keys (rows past Lp are zero)
+  for (int i = tid; i < KT * DQK / 16; i += NT) {
+    const int r = (i * 16) / DQK, c = ((i * 16) % DQK) / 16;
+    v4i x = v4i{};
+    if (k0 + r < Lp) x = *reinterpret_cast<const v4i*>(kc + (khead * Lp + k0 + r) * DQK + 16 * c);
+    *reinterpret_cast<v4i*>(lds + C::K_OFF + r * DQK + 16 * tile_slot<DQK>(r, c)) = x;
   }
-  for (int i = tid; i < 128 * DV / 16; i += kThreads) {
-    const int r = (i * 16) / DV, c = (i * 16) % DV;
-    *reinterpret_cast<v4i*>(kv.v + r * KV::VROW + c) = *reinterpret_cast<const v4i*>(vc + (khead * Lp + k0 + r) * DV + c);
+  for (int i = tid; i < KT * DV / 16; i += NT) {
+    const int r = (i * 16) / DV, c = ((i * 16) % DV) / 16;
+    v4i x = v4i{};
+    if (k0 + r < Lp) x = *reinterpret_cast<const v4i*>(vc + (khead * Lp + k0 + r) * DV + 16 * c);
+    *reinterpret_cast<v4i*>(lds + C::V_OFF + r * DV + 16 * tile_slot<DV>(r, c)) = x;
   }
-  for (int i = tid; i < 128 * KB; i += kThreads) kv.ksc[i] = kcs[(khead * Lp + k0) * KB + i];
-  for (int i = tid; i < 128 * VB; i += kThreads) kv.vsc[i] = vcs[(khead * Lp + k0) * VB + i];
+  for (int i = tid; i < KT * KB; i += NT)
+    reinterpret_cast<float*>(lds + C::KS_OFF)[i] = (k0 + i / KB < Lp) ? kcs[(khead * Lp + k0) * KB + i] : 1.f;
+  for (int i = tid; i < KT * VB; i += NT)
+    reinterpret_cast<float*>(lds + C::VS_OFF)[i] = (k0 + i / VB < Lp) ? vcs[(khead * Lp + k0) * VB + i] : 1.f;
 
-  v16f dkacc[NKW], dvacc[NVW];
+  // ---- per-lane source offsets of this wave's direct loads (loop invariant)
+  int doff[C::NDW];
 #pragma unroll
-  for (int i = 0; i < NKW; ++i) dkacc[i] = v16f{};
+  for (int i = 0; i < C::NDW; ++i) {
+    const int j = w + NW * i;
+    const int pb = j * 1024 + 16 * lane;             // stage byte this lane fills
+    int off = 0;
+    if (pb < C::DOC) {
+      const int p = pb - C::QC, r = p / DQK, c = (p % DQK) / 16;
+      off = r < kBQ ? r * DQK + 16 * tile_slot<DQK>(r, c) : -1;
+    } else if (pb < C::QS) {
+      const int p = pb - C::DOC, r = p / DV, c = (p % DV) / 16;
+      off = r < kBQ ? r * DV + 16 * tile_slot<DV>(r, c) : -1;
+    } else if (pb < C::DOS) {
+      const int p = pb - C::QS, r = p / 64, c = (p % 64) / 16;   // r: channel within the instruction's 16
+      off = r < DQK ? (r % 16) * Lp + 16 * tile_slot<64>(r, c) : -1;
+    } else if (pb < C::QCS) {
+      const int p = pb - C::DOS, r = p / 64, c = (p % 64) / 16;
+      off = r < DV ? (r % 16) * Lp + 16 * tile_slot<64>(r, c) : -1;
+    } else if (pb < C::DOCS) {
+      const int p = pb - C::QCS, pos = p / (4 * KB), within = p % (4 * KB);
+      off = pos < kBQ ? ((pos & ~31) + pair_row(pos & 31)) * 4 * KB + within : -1;
+    } else {
+      const int p = pb - C::DOCS, pos = p / (4 * VB), within = p % (4 * VB);
+      off = pos < kBQ ? ((pos & ~31) + pair_row(pos & 31)) * 4 * VB + within : -1;
+    }
+    doff[i] = off;
+  }
+  // issue the direct loads of step (qhead, q0) into stage buffer st
+  auto issue_stage = [&](int64_t qhead, int q0, uint8_t* st) {
 #pragma unroll
-  for (int i = 0; i < NVW; ++i) dvacc[i] = v16f{};
+    for (int i = 0; i < C::NDW; ++i) {
+      const int j = w + NW * i;
+      if (j >= C::NDMA) continue;
+      const int jb = j * 1024;
+      const uint8_t* base;
+      if (jb < C::DOC) base = qc + (qhead * Lp + q0) * DQK;
+      else if (jb < C::QS) base = doc + (qhead * Lp + q0) * DV;
+      else if (jb < C::DOS) base = qs + (qhead * DQK + (jb - C::QS) / 64) * (int64_t)Lp + q0;
+      else if (jb < C::QCS) base = dos + (qhead * DV + (jb - C::DOS) / 64) * (int64_t)Lp + q0;
+      else if (jb < C::DOCS) base = reinterpret_cast<const uint8_t*>(qcs + (qhead * Lp + q0) * KB);
+      else base = reinterpret_cast<const uint8_t*>(docs + (qhead * Lp + q0) * VB);
+      if (doff[i] >= 0) dma16(base + doff[i], st + jb);
+    }
+  };
+  // the step's small items (Q^<s>, dO^<s> scales of its two query blocks, LSE, delta) via registers
+  float smallv[C::NSR];
+  auto load_small = [&](int64_t qhead, int q0) {
+#pragma unroll
+    for (int i = 0; i < C::NSR; ++i) {
+      const int e = tid + NT * i;
+      float x = 0.f;
+      if (e < DQK * 2) {
+        x = qss[(qhead * DQK + e / 2) * LB + q0 / kBlock + (e & 1)];
+      } else if (e < DQK * 2 + DV * 2) {
+        const int f = e - DQK * 2;
+        x = doss[(qhead * DV + f / 2) * LB + q0 / kBlock + (f & 1)];
+      } else if (e < DQK * 2 + DV * 2 + kBQ) {
+        const int q = q0 + e - DQK * 2 - DV * 2;
+        x = q < L ? lse[qhead * L + q] * kLog2e : INFINITY;    // padded queries: P = 0
+      } else if (e < C::NSMALL) {
+        const int q = q0 + e - DQK * 2 - DV * 2 - kBQ;
+        x = q < L ? delta[qhead * L + q] : 0.f;
+      }
+      smallv[i] = x;
+    }
+  };
+  auto store_small = [&](uint8_t* st) {
+#pragma unroll
+    for (int i = 0; i < C::NSR; ++i) {
+      const int e = tid + NT * i;
+      if (e < C::NSMALL) reinterpret_cast<float*>(st + C::QSS)[e] = smallv[i];
+    }
+  };
+
+  v16f dkacc[NKT], dvacc[NVT];
+#pragma unroll
+  for (int i = 0; i < NKT; ++i) dkacc[i] = v16f{};
+#pragma unroll
+  for (int i = 0; i < NVT; ++i) dvacc[i] = v16f{};
 
   const float c2 = sigma * kLog2e;
-  const int arow = 32 * qh + pair_row(R);
   const int qstart = CAUSAL ? k0 : 0;
-  const int nsteps = (Lp - qstart) / kBQ;
+  const int nsteps = qstart < Lp ? (Lp - qstart) / kBQ : 0;
   const int total = G * nsteps;
+  const int64_t qhead0 = (int64_t)b * Hq + (int64_t)hk * G;
+  const int prow = pair_row(R);
+  // LDS read offsets of this lane.  Each tile map depends only on row bits that a
+  // 32-row (or 32-channel) step leaves unchanged, so tiles j / channel tiles ct
+  // are plain immediate offsets from these.
+  int oq[KS][2], od[VS][2], ok[KS][2], ov[VS][2], ot[2];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      oq[ks][e] = prow * DQK + 16 * tile_slot<DQK>(prow, 4 * ks + 2 * e + h);
+      ok[ks][e] = (32 * w + R) * DQK + 16 * tile_slot<DQK>(R, 4 * ks + 2 * e + h);
+    }
+#pragma unroll
+  for (int ks = 0; ks < VS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      od[ks][e] = prow * DV + 16 * tile_slot<DV>(prow, 4 * ks + 2 * e + h);
+      ov[ks][e] = (32 * w + R) * DV + 16 * tile_slot<DV>(R, 4 * ks + 2 * e + h);
+    }
+#pragma unroll
+  for (int e = 0; e < 2; ++e) ot[e] = R * kBQ + 16 * tile_slot<64>(R, 2 * e + h);
 
-  Prefetch<DQK, DV> pf;
-  prefetch<DQK, DV>(pf, tid, (int64_t)b * Hq + hk * G, qstart, L, Lp, qc, qcs, qs, qss, doc, docs, dos, doss, lse,
-                    delta);
-  commit<DQK, DV>(pf, sm, tid);
-  __syncthreads();
-
+  if (total > 0) {
+    issue_stage(qhead0, qstart, stage0);
+    load_small(qhead0, qstart);
+    store_small(stage0);
+  }
   for (int it = 0; it < total; ++it) {
     const int hh = it / nsteps;
     const int q0 = qstart + (it - hh * nsteps) * kBQ;
-    if (it + 1 < total) {
+    uint8_t* const st = stage0 + (it & 1) * C::STAGE;
+    uint8_t* const stn = stage0 + ((it + 1) & 1) * C::STAGE;
+    wait_vmem();
+    __syncthreads();                               // step it staged; buffer (it+1)&1 free
+    const bool more = it + 1 < total;
+    if (more) {
       const int hn = (it + 1) / nsteps;
-      prefetch<DQK, DV>(pf, tid, (int64_t)b * Hq + hk * G + hn, qstart + (it + 1 - hn * nsteps) * kBQ, L, Lp, qc,
-                        qcs, qs, qss, doc, docs, dos, doss, lse, delta);
+      const int qn = qstart + (it + 1 - hn * nsteps) * kBQ;
+      issue_stage(qhead0 + hn, qn, stn);
+      load_small(qhead0 + hn, qn);
     }
 
-    // ---- A: S and dP^ tiles; lane (key R, h), register v <-> query 32*qh + 16*h + v
-    v16f s = v16f{}, dp = v16f{};
+    if (kw0 < L && (!CAUSAL || q0 + kBQ - 1 >= kw0)) {
+      const bool need_mask = (kw0 + 32 > L) || (CAUSAL && q0 < kw0 + 31);
+      // this wave's K and V rows are the B operands (lane R = key, K-slots = channels)
+      const float* ksr = reinterpret_cast<const float*>(lds + C::KS_OFF) + (32 * w + R) * KB;
+      const float* vsr = reinterpret_cast<const float*>(lds + C::VS_OFF) + (32 * w + R) * VB;
+      v4i pcode[2], dcode[2];
+      int pscl[2], dscl[2];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint8_t* p = sm.q + arow * SM::QROW + 64 * ks;
-      const uint8_t* pk = kv.k + kr * KV::KROW + 64 * ks;
-      v8i a = cat(lds_read16(p + 16 * h), lds_read16(p + 32 + 16 * h));
-      v8i bk = cat(lds_read16(pk + 16 * h), lds_read16(pk + 32 + 16 * h));
-      s = mfma<E4M3, E4M3>(a, bk, s, e8m0(sm.qsc[arow * KB + 2 * ks + h]), e8m0(kv.ksc[kr * KB + 2 * ks + h]));
-    }
+      for (int j = 0; j < 2; ++j) {
+        // S^T and dP^T for queries 32j .. 32j+31 of the step (rows in pair_row order)
+        const uint8_t* qt = st + C::QC + 32 * j * DQK;
+        const uint8_t* dt = st + C::DOC + 32 * j * DV;
+        const float* qsr = reinterpret_cast<const float*>(st + C::QCS) + (32 * j + R) * KB;
+        const float* dsr = reinterpret_cast<const float*>(st + C::DOCS) + (32 * j + R) * VB;
+        v16f s = v16f{}, dp = v16f{};
 #pragma unroll
-    for (int ks = 0; ks < VS; ++ks) {
-      const uint8_t* p = sm.dO + arow * SM::VROW + 64 * ks;
-      const uint8_t* pv = kv.v + kr * KV::VROW + 64 * ks;
-      v8i a = cat(lds_read16(p + 16 * h), lds_read16(p + 32 + 16 * h));
-      v8i bv = cat(lds_read16(pv + 16 * h), lds_read16(pv + 32 + 16 * h));
-      dp = mfma<E5M2, E4M3>(a, bv, dp, e8m0(sm.dOsc[arow * VB + 2 * ks + h]), e8m0(kv.vsc[kr * VB + 2 * ks + h]));
-    }
-    const bool need_mask = (k0 + 128 > L) || (CAUSAL && q0 < k0 + 128);
-    const int qb = 32 * qh + 16 * h;               // first step-query of this lane's 16
+        for (int ks = 0; ks < KS; ++ks) {
+          const v8i a = cat(lds_read16(qt + oq[ks][0]), lds_read16(qt + oq[ks][1]));
+          const v8i bk = cat(lds_read16(lds + C::K_OFF + ok[ks][0]), lds_read16(lds + C::K_OFF + ok[ks][1]));
+          s = mfma<E4M3, E4M3>(a, bk, s, e8m0(qsr[2 * ks + h]), e8m0(ksr[2 * ks + h]));
+        }
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const v4f l4 = *reinterpret_cast<const v4f*>(sm.lse + qb + 4 * g);
-      const v4f d4 = *reinterpret_cast<const v4f*>(sm.del + qb + 4 * g);
+        for (int ks = 0; ks < VS; ++ks) {
+          const v8i a = cat(lds_read16(dt + od[ks][0]), lds_read16(dt + od[ks][1]));
+          const v8i bv = cat(lds_read16(lds + C::V_OFF + ov[ks][0]), lds_read16(lds + C::V_OFF + ov[ks][1]));
+          dp = mfma<E5M2, E4M3>(a, bv, dp, e8m0(dsr[2 * ks + h]), e8m0(vsr[2 * ks + h]));
+        }
+        // lane (key R, h), register v <-> step query 32j + 16h + v
+        const float* l2p = reinterpret_cast<const float*>(st + C::LSE) + 32 * j + 16 * h;
+        const float* dlp = reinterpret_cast<const float*>(st + C::DEL) + 32 * j + 16 * h;
+        if (need_mask) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int v = 4 * g + e;
-        float x = s[v];
-        if (need_mask && (key >= L || (CAUSAL && key > q0 + qb + v))) x = -INFINITY;
-        const float p = __builtin_amdgcn_exp2f(fmaf(x, c2, -l4[e]));
-        s[v] = p;                                   // s now holds P
-        dp[v] = p * (dp[v] - d4[e]);                // dp now holds dS
+          for (int v = 0; v < 16; ++v) {
+            const int q = q0 + 32 * j + 16 * h + v;
+            if (key >= L || (CAUSAL && key > q)) s[v] = -INFINITY;
+          }
+        }
+        float am = 0.f, dm = 0.f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const v4f l4 = *reinterpret_cast<const v4f*>(l2p + 4 * g);
+          const v4f d4 = *reinterpret_cast<const v4f*>(dlp + 4 * g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int v = 4 * g + e;
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[v], c2, -l4[e]));
+            const float d = p * (dp[v] - d4[e]);
+            s[v] = p;                                 // s now holds P
+            dp[v] = d;                                // dp now holds dS
+            am = fmaxf(am, p);
+            dm = fmaxf(dm, fabsf(d));
+          }
+        }
+        am = pair_max(am);
+        dm = pair_max(dm);
+        const int kp = scale_exp<E4M3>(am), kd = scale_exp<E5M2>(dm);
+        const float sp = exp2i(kp), sd = exp2i(kd);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          pcode[j][g] = (int)pack4s<E4M3>(s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3], sp);
+          dcode[j][g] = (int)pack4s<E5M2>(dp[4 * g], dp[4 * g + 1], dp[4 * g + 2], dp[4 * g + 3], sd);
+        }
+        pscl[j] = kp + 127;
+        dscl[j] = kd + 127;
+        __builtin_amdgcn_sched_barrier(0);          // bound the live operand tiles (register budget)
       }
-    }
-    {
-      // P^<q>, dS^<q>: this wave's 32 queries form one block per key (lane pair)
-      float am = 0.f, dm = 0.f;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        am = fmaxf(am, s[v]);
-        dm = fmaxf(dm, fabsf(dp[v]));
-      }
-      am = pair_max(am);
-      dm = pair_max(dm);
-      const int kp = scale_exp<E4M3>(am), kd = scale_exp<E5M2>(dm);
-      const float sp = exp2i(kp), sd = exp2i(kd);
-      v4i pw, dw;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        pw[g] = (int)pack4s<E4M3>(s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3], sp);
-        dw[g] = (int)pack4s<E5M2>(dp[4 * g], dp[4 * g + 1], dp[4 * g + 2], dp[4 * g + 3], sd);
-      }
-      const int slot = (kg * 2 + qh) * 64 + lane;
-      sm.pc[slot] = pw;
-      sm.dc[slot] = dw;
-      sm.psc[slot] = kp + 127;
-      sm.dsc[slot] = kd + 127;
-    }
-    __syncthreads();
 
-    // ---- B: dV^T and dK^T over the step's 64 queries (both query halves of key group kg)
-    {
-      const int s0 = (kg * 2 + 0) * 64 + lane, s1 = (kg * 2 + 1) * 64 + lane;
-      const v8i pq = cat(sm.pc[s0], sm.pc[s1]);
-      const v8i dsq = cat(sm.dc[s0], sm.dc[s1]);
-      const int psc = sm.psc[(kg * 2 + h) * 64 + lane];
-      const int dsc = sm.dsc[(kg * 2 + h) * 64 + lane];
+      // dV^T += dO^<s>^T P^<q>, dK^T += Q^<s>^T dS^<q> over the step's 64 queries.
+      // B operand: lane (key R, h) holds queries 16h.. of tile 0 and of tile 1.
+      const v8i pq = cat(pcode[0], pcode[1]);
+      const v8i dsq = cat(dcode[0], dcode[1]);
+      const int psc = h ? pscl[1] : pscl[0];
+      const int dsc = h ? dscl[1] : dscl[0];
+      const float* qssr = reinterpret_cast<const float*>(st + C::QSS);
+      const float* dossr = reinterpret_cast<const float*>(st + C::DOSS);
 #pragma unroll
-      for (int m = 0; m < NVW; ++m) {
-        const int ch = 32 * (qh + 2 * m) + R;
-        const uint8_t* p = sm.dOt + ch * SM::TROW;
-        v8i a = cat(lds_read16(p + 16 * h), lds_read16(p + 32 + 16 * h));
-        dvacc[m] = mfma<E5M2, E4M3>(a, pq, dvacc[m], e8m0(sm.dOtsc[ch * 2 + h]), psc);
+      for (int ct = 0; ct < NVT; ++ct) {
+        const int ch = 32 * ct + R;
+        const uint8_t* p = st + C::DOS + 32 * ct * kBQ;
+        const v8i a = cat(lds_read16(p + ot[0]), lds_read16(p + ot[1]));
+        dvacc[ct] = mfma<E5M2, E4M3>(a, pq, dvacc[ct], e8m0(dossr[2 * ch + h]), psc);
       }
 #pragma unroll
-      for (int m = 0; m < NKW; ++m) {
-        const int ch = 32 * (qh + 2 * m) + R;
-        const uint8_t* p = sm.qt + ch * SM::TROW;
-        v8i a = cat(lds_read16(p + 16 * h), lds_read16(p + 32 + 16 * h));
-        dkacc[m] = mfma<E4M3, E5M2>(a, dsq, dkacc[m], e8m0(sm.qtsc[ch * 2 + h]), dsc);
+      for (int ct = 0; ct < NKT; ++ct) {
+        const int ch = 32 * ct + R;
+        const uint8_t* p = st + C::QS + 32 * ct * kBQ;
+        const v8i a = cat(lds_read16(p + ot[0]), lds_read16(p + ot[1]));
+        dkacc[ct] = mfma<E4M3, E5M2>(a, dsq, dkacc[ct], e8m0(qssr[2 * ch + h]), dsc);
       }
     }
-    __syncthreads();
-    // every read of this step's staging buffers is done: the next step's operands go in
-    if (it + 1 < total) {
-      commit<DQK, DV>(pf, sm, tid);
-      __syncthreads();
-    }
+    if (more) store_small(stn);
   }
 
-  // ---- dK, dV written once per key: wave (kg, qh) holds channel tiles qh, qh+2, ...
+  // ---- dK, dV written once per key: register v of channel tile ct <-> channel 32ct + 8(v/4) + 4h + v%4
   if (key < L) {
     float* dkr = dk + (khead * L + key) * DQK + 4 * h;
     float* dvr = dv + (khead * L + key) * DV + 4 * h;
 #pragma unroll
-    for (int m = 0; m < NKW; ++m)
+    for (int ct = 0; ct < NKT; ++ct)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        v4f r = {sigma * dkacc[m][4 * a], sigma * dkacc[m][4 * a + 1], sigma * dkacc[m][4 * a + 2],
-                 sigma * dkacc[m][4 * a + 3]};
-        *reinterpret_cast<v4f*>(dkr + 32 * (qh + 2 * m) + 8 * a) = r;
+        v4f r = {sigma * dkacc[ct][4 * a], sigma * dkacc[ct][4 * a + 1], sigma * dkacc[ct][4 * a + 2],
+                 sigma * dkacc[ct][4 * a + 3]};
+        *reinterpret_cast<v4f*>(dkr + 32 * ct + 8 * a) = r;
       }
 #pragma unroll
-    for (int m = 0; m < NVW; ++m)
+    for (int ct = 0; ct < NVT; ++ct)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        v4f r = {dvacc[m][4 * a], dvacc[m][4 * a + 1], dvacc[m][4 * a + 2], dvacc[m][4 * a + 3]};
-        *reinterpret_cast<v4f*>(dvr + 32 * (qh + 2 * m) + 8 * a) = r;
+        v4f r = {dvacc[ct][4 * a], dvacc[ct][4 * a + 1], dvacc[ct][4 * a + 2], dvacc[ct][4 * a + 3]};
+        *reinterpret_cast<v4f*>(dvr + 32 * ct + 8 * a) = r;
       }
   }
 }
@@ -317,20 +343,20 @@ __global__ __launch_bounds__(kThreads) void dkdv_kernel(
 template <int DQK, int DV>
 static void launch_dkdv_t(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand vc, Operand doc,
                           Operand dos, const float* lse, const float* delta, float* dk, float* dv, hipStream_t s) {
-  dim3 grid(d.Lp / 128, d.Hkv, d.B);
+  using C = DkdvCfg<DQK, DV>;
+  dim3 grid(d.Hkv, d.B, (d.Lp + C::KT - 1) / C::KT);
   if (d.causal)
-    hipLaunchKernelGGL((dkdv_kernel<DQK, DV, true>), grid, dim3(kThreads), 0, s, qc.codes, qc.scales, qs.codes,
+    hipLaunchKernelGGL((dkdv_kernel<DQK, DV, true>), grid, dim3(C::NT), 0, s, qc.codes, qc.scales, qs.codes,
                        qs.scales, kc.codes, kc.scales, vc.codes, vc.scales, doc.codes, doc.scales, dos.codes,
                        dos.scales, lse, delta, dk, dv, d.Hq, d.Hkv, d.L, d.Lp, d.sigma);
   else
-    hipLaunchKernelGGL((dkdv_kernel<DQK, DV, false>), grid, dim3(kThreads), 0, s, qc.codes, qc.scales, qs.codes,
+    hipLaunchKernelGGL((dkdv_kernel<DQK, DV, false>), grid, dim3(C::NT), 0, s, qc.codes, qc.scales, qs.codes,
                        qs.scales, kc.codes, kc.scales, vc.codes, vc.scales, doc.codes, doc.scales, dos.codes,
                        dos.scales, lse, delta, dk, dv, d.Hq, d.Hkv, d.L, d.Lp, d.sigma);
 }
 
-hipError_t launch_bwd(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand ks, Operand vc, Operand doc,
-                      Operand dos, const float* lse, const float* delta, float* dq, float* dk, float* dv,
-                      double* ps, double* pa, hipStream_t s) {
+hipError_t launch_dkdv(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand vc, Operand doc, Operand dos,
+                       const float* lse, const float* delta, float* dk, float* dv, hipStream_t s) {
   if (d.dqk == 64 && d.dv == 64) launch_dkdv_t<64, 64>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);
   else if (d.dqk == 128 && d.dv == 128) launch_dkdv_t<128, 128>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);
   else if (d.dqk == 192 && d.dv == 128) launch_dkdv_t<192, 128>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);
@@ -338,7 +364,13 @@ hipError_t launch_bwd(const AttnDims& d, Operand qc, Operand qs, Operand kc, Ope
   else if (d.dqk == 128 && d.dv == 64) launch_dkdv_t<128, 64>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);
   else if (d.dqk == 192 && d.dv == 64) launch_dkdv_t<192, 64>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);
   else return hipErrorInvalidValue;
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand ks, Operand vc, Operand doc,
+                      Operand dos, const float* lse, const float* delta, float* dq, float* dk, float* dv,
+                      double* ps, double* pa, hipStream_t s) {
+  hipError_t e = launch_dkdv(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);
   if (e != hipSuccess) return e;
   return launch_dq(d, qc, kc, ks, vc, doc, lse, delta, dq, ps, pa, s);
 }

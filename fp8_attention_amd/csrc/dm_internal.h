@@ -31,6 +31,9 @@ hipError_t launch_bwd(const AttnDims& d, Operand q_c, Operand q_s, Operand k_c, 
                       Operand do_c, Operand do_s, const float* lse, const float* delta, float* dq, float* dk,
                       float* dv, double* probe_sum, double* probe_abs, hipStream_t s);
 
+hipError_t launch_dkdv(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand vc, Operand doc, Operand dos,
+                       const float* lse, const float* delta, float* dk, float* dv, hipStream_t s);
+
 hipError_t launch_dq(const AttnDims& d, Operand qc, Operand kc, Operand ks, Operand vc, Operand doc,
                      const float* lse, const float* delta, float* dq, double* ps, double* pa, hipStream_t s);
 

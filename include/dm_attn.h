@@ -159,6 +159,26 @@ dm_status dm_attn_bwd(const dm_attn_shape* shape, dm_fp8_operand q_c, dm_fp8_ope
                       const float* delta, float* dq, float* dk, float* dv,
                       double* probe_rowsum_ds, double* probe_rowsum_abs_pdp, hipStream_t stream);
 
+/*
+ * The two independent halves of dm_attn_bwd, for callers that time them apart
+ * or run them on two streams (same arguments, same results; neither reads what
+ * the other writes).  dm_attn_bwd is dm_attn_bwd_dkdv followed by
+ * dm_attn_bwd_dq on one stream.
+ *   dm_attn_bwd_dkdv: dK and dV (key-stationary; the section 03 products
+ *     P^<q>^T dO^<s> and dS^<q>^T Q^<s>); needs q_c, q_s, k_c, v_c, do_c, do_s.
+ *   dm_attn_bwd_dq: dQ and the optional row-sum probes (query-stationary; the
+ *     product dS^<k> K^<s>); needs q_c, k_c, k_s, v_c, do_c.
+ * Errors as for dm_attn_bwd.
+ */
+dm_status dm_attn_bwd_dkdv(const dm_attn_shape* shape, dm_fp8_operand q_c, dm_fp8_operand q_s,
+                           dm_fp8_operand k_c, dm_fp8_operand v_c, dm_fp8_operand do_c,
+                           dm_fp8_operand do_s, const float* lse, const float* delta, float* dk,
+                           float* dv, hipStream_t stream);
+dm_status dm_attn_bwd_dq(const dm_attn_shape* shape, dm_fp8_operand q_c, dm_fp8_operand k_c,
+                         dm_fp8_operand k_s, dm_fp8_operand v_c, dm_fp8_operand do_c,
+                         const float* lse, const float* delta, float* dq,
+                         double* probe_rowsum_ds, double* probe_rowsum_abs_pdp, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

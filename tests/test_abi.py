@@ -116,6 +116,19 @@ def test_bwd_probe_pointers_come_in_pairs():
     assert lib.dm_attn_bwd(ctypes.byref(s), *ops, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None) == _lib.DM_ERR_SHAPE
 
 
+def test_split_backward_validation():
+    lib = _lib.load()
+    s = AttnShape(1, 2, 2, 128, 128, 128, True).c()
+    op = _op()
+    assert lib.dm_attn_bwd_dkdv(ctypes.byref(s), *[op] * 6, FAKE, FAKE, FAKE, None, None) == _lib.DM_ERR_NULL
+    assert lib.dm_attn_bwd_dkdv(ctypes.byref(s), *[op] * 6, FAKE, FAKE, FAKE, MIS, None) == _lib.DM_ERR_ALIGN
+    assert lib.dm_attn_bwd_dq(ctypes.byref(s), *[op] * 5, FAKE, FAKE, FAKE, FAKE, None, None) == _lib.DM_ERR_NULL
+    assert lib.dm_attn_bwd_dq(ctypes.byref(s), *[op] * 5, FAKE, FAKE, MIS, None, None, None) == _lib.DM_ERR_ALIGN
+    s.d_qk = 96
+    assert lib.dm_attn_bwd_dkdv(ctypes.byref(s), *[op] * 6, FAKE, FAKE, FAKE, FAKE, None) == _lib.DM_ERR_SHAPE
+    assert lib.dm_attn_bwd_dq(ctypes.byref(s), *[op] * 5, FAKE, FAKE, FAKE, None, None, None) == _lib.DM_ERR_SHAPE
+
+
 def test_quantize_validation():
     lib = _lib.load()
     q = lib.dm_quantize_blockfp8
