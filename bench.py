@@ -77,6 +77,25 @@ def cpu_baseline(w, inputs, rows: int) -> dict:
                       f"that sample / wall time; numpy FP64"}
 
 
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 counter summary, or None when the
+    summary is for another workload or the kernel's sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    k = rec.get("kernels", {}).get(kernel)
+    if rec.get("workload") != workload or k is None:
+        return None
+    h = hashlib.sha256()
+    for f in k["sources"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != k["sha256"]:
+        return None
+    return k["hbm_read_bytes"] + k["hbm_write_bytes"]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -207,7 +226,7 @@ def main():
                    "delta_mode": "matched", "step": "fwd + matched delta + bwd on pre-quantized operands",
                    "pct_fp8_peak": 100 * value / PEAK_FP8_TFLOPS},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                     "frac": ach / PEAK_FP8_TFLOPS, "traffic": None},
+                     "frac": ach / PEAK_FP8_TFLOPS, "traffic": measured_traffic(w.name, dom)},
         "kernels": extra,
         "cpu_baseline": cpu,
     }
