@@ -15,6 +15,8 @@ dm_status check_shape(const dm_attn_shape* s) {
   if (s->batch < 1 || s->heads_q < 1 || s->heads_kv < 1 || s->seqlen < 0) return DM_ERR_SHAPE;
   if (s->batch > 65535 || s->heads_q > 65535 || s->seqlen > (1 << 26)) return DM_ERR_SHAPE;
   if (s->heads_q % s->heads_kv != 0) return DM_ERR_SHAPE;
+  // every kernel grid is one-dimensional over (sequence tile of 128, head, batch)
+  if ((int64_t)s->batch * s->heads_q * ((s->seqlen + 127) / 128) > INT32_MAX) return DM_ERR_SHAPE;
   if (s->d_qk != 64 && s->d_qk != 128 && s->d_qk != 192) return DM_ERR_SHAPE;
   if (s->d_v != 64 && s->d_v != 128) return DM_ERR_SHAPE;
   if (s->causal != 0 && s->causal != 1) return DM_ERR_SHAPE;

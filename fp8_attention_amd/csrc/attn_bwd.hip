@@ -1,8 +1,8 @@
 // dK and dV of block-scaled FP8 attention (key-stationary).
 //
 // Workgroup = NW waves, wave w owning keys k0+32w .. k0+32w+31 and every channel;
-// grid = (Hkv, B, key tiles), key tiles slowest so the long causal tiles start
-// first.  The workgroup walks the query heads of its KV group and, for each, the
+// a 1-D grid over (key tile, Hkv, B) with key tiles slowest, so the long causal
+// tiles start first.  The workgroup walks the query heads of its KV group and, for each, the
 // 64-query steps that can see its keys.  Per step and wave:
 //   S^T = Q K^T and dP^T = dO V^T for two 32-query tiles (scaled FP8 MFMA; one key
 //   per lane pair, 16 queries per lane); P = exp(S - LSE), dS = P (dP^ - delta)
@@ -71,8 +71,10 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int R = lane & 31, h = lane >> 5;
-  const int hk = blockIdx.x, b = blockIdx.y;
-  const int k0 = blockIdx.z * KT;
+  const int nkt = (Lp + KT - 1) / KT;
+  const int nhb = Hkv * (int)(gridDim.x / (nkt * Hkv));    // Hkv * B
+  const int hk = (int)blockIdx.x % nhb % Hkv, b = (int)blockIdx.x % nhb / Hkv;
+  const int k0 = ((int)blockIdx.x / nhb) * KT;            // key tiles slowest: long causal tiles first
   const int G = Hq / Hkv;
   const int kw0 = k0 + 32 * w;                       // this wave's first key
   const int key = kw0 + R;                           // this lane's key (column of the S^T tiles)
@@ -344,7 +346,7 @@ template <int DQK, int DV>
 static void launch_dkdv_t(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand vc, Operand doc,
                           Operand dos, const float* lse, const float* delta, float* dk, float* dv, hipStream_t s) {
   using C = DkdvCfg<DQK, DV>;
-  dim3 grid(d.Hkv, d.B, (d.Lp + C::KT - 1) / C::KT);
+  dim3 grid((unsigned)((d.Lp + C::KT - 1) / C::KT) * d.Hkv * d.B);
   if (d.causal)
     hipLaunchKernelGGL((dkdv_kernel<DQK, DV, true>), grid, dim3(C::NT), 0, s, qc.codes, qc.scales, qs.codes,
                        qs.scales, kc.codes, kc.scales, vc.codes, vc.scales, doc.codes, doc.scales, dos.codes,

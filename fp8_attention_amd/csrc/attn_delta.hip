@@ -5,9 +5,10 @@
 //   O and x with 16-byte loads; bound by HBM bandwidth.
 // matched (Delta-Matching): delta_i = sum_j P_ij dP^_ij with P = exp(S - LSE)
 //   recomputed in FP32 and dP^ = dO^<c> V^<c>^T on FP8 matrix cores.  Same tiling
-//   as the forward: 4 waves x 32 queries, 128-key chunks staged in LDS; the S^T
-//   and dP^T tiles share one layout (query per lane pair, 16 keys per lane), so
-//   the product and its row sum stay in registers until one pair reduction.
+//   as the forward: 8 waves x 32 queries, 128-key chunks streamed through LDS;
+//   the S^T and dP^T tiles share one layout (query per lane pair, 16 keys per
+//   lane), so the product and its row sum stay in registers until one pair
+//   reduction.
 #include "dm_common.h"
 #include "dm_internal.h"
 
@@ -84,108 +85,191 @@ hipError_t launch_delta_rows(const AttnDims& d, int mode, const float* o, const 
 // ---------------------------------------------------------------------------
 // matched
 // ---------------------------------------------------------------------------
+constexpr int kDelWaves = 8;
+constexpr int kDelQ = 32 * kDelWaves;    // queries per workgroup
+
+template <int DQK, int DV>
+struct DeltaLds {
+  static constexpr int KB = DQK / 32, VB = DV / 32;
+  static constexpr int K = kChunk * DQK, V = kChunk * DV;      // K^<c>, V^<c> rows of a chunk, swizzled
+  static constexpr int KS = kChunk * KB * 4, VS = kChunk * VB * 4;
+  static constexpr int BUF = K + V + KS + VS;                  // one chunk
+  static constexpr int OFF_V = K, OFF_KS = K + V, OFF_VS = K + V + KS;
+  static constexpr int NJ = BUF / 1024;                        // direct loads per chunk
+  static constexpr int NJW = (NJ + kDelWaves - 1) / kDelWaves;
+  static_assert(K % 1024 == 0 && V % 1024 == 0 && KS % 1024 == 0 && VS % 1024 == 0, "whole 1 KB loads");
+};
+
+// Workgroup = 8 waves = 256 queries; 1-D grid over (query tile, Hq, B), query
+// tile slowest and the longest causal tiles first.  Per 128-key chunk and 32-key tile:
+// S^T = K Q^T and dP^T = V dO^T (lane pair = query, 16 keys per lane), then
+// delta += sum P * dP^ with P = exp2(S sigma log2e - LSE log2e).  The tiles of
+// chunk c+1 are computed as soon as tile t of chunk c has been consumed; K^<c> /
+// V^<c> chunks are double-buffered in LDS via direct global->LDS loads.
 template <int DQK, int DV, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void delta_matched_kernel(
+__global__ __launch_bounds__(64 * kDelWaves) void delta_matched_kernel(
     const uint8_t* __restrict__ qc, const float* __restrict__ qcs, const uint8_t* __restrict__ kc,
     const float* __restrict__ kcs, const uint8_t* __restrict__ vc, const float* __restrict__ vcs,
     const uint8_t* __restrict__ doc, const float* __restrict__ docs, const float* __restrict__ lse,
     float* __restrict__ delta, int Hq, int Hkv, int L, int Lp, float sigma) {
+  using C = DeltaLds<DQK, DV>;
   constexpr int KS = DQK / 64, VS = DV / 64;
   constexpr int KB = DQK / 32, VB = DV / 32;
-  constexpr int KROW = DQK + 16, VROW = DV + 16;
-  __shared__ __attribute__((aligned(16))) uint8_t sK[kChunk * KROW];
-  __shared__ __attribute__((aligned(16))) float sKs[kChunk * KB];
-  __shared__ __attribute__((aligned(16))) uint8_t sV[kChunk * VROW];
-  __shared__ __attribute__((aligned(16))) float sVs[kChunk * VB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::BUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int R = lane & 31, h = lane >> 5;
-  const int nqt = Lp / kChunk;
-  const int qt = CAUSAL ? (nqt - 1 - (int)blockIdx.x) : (int)blockIdx.x;
-  const int hq = blockIdx.y, b = blockIdx.z;
+  const int nqt = (Lp + kDelQ - 1) / kDelQ;
+  const int nhb = Hq * (int)(gridDim.x / (nqt * Hq));      // Hq * B
+  const int tr = (int)blockIdx.x / nhb, hb = (int)blockIdx.x % nhb;
+  const int qt = CAUSAL ? (nqt - 1 - tr) : tr;            // longest causal tiles dispatched first
+  const int hq = hb % Hq, b = hb / Hq;
   const int hk = hq / (Hq / Hkv);
-  const int q0 = qt * kChunk;
-  const int qi = q0 + 32 * w + R;
+  const int q0 = qt * kDelQ;
+  const int qw = q0 + 32 * w;
+  const bool live = qw < Lp;
+  const int qi = qw + R;
   const int64_t qhead = (int64_t)b * Hq + hq, khead = (int64_t)b * Hkv + hk;
-  const uint8_t* Qc = qc + qhead * Lp * DQK;
-  const float* Qcs = qcs + qhead * Lp * KB;
-  const uint8_t* dOc = doc + qhead * Lp * DV;
-  const float* dOcs = docs + qhead * Lp * VB;
   const uint8_t* Kc = kc + khead * Lp * DQK;
   const float* Kcs = kcs + khead * Lp * KB;
   const uint8_t* Vc = vc + khead * Lp * DV;
   const float* Vcs = vcs + khead * Lp * VB;
 
+  // direct-load source offsets (relative to the chunk) of this lane, loop invariant
+  int soff[C::NJW];
+#pragma unroll
+  for (int i = 0; i < C::NJW; ++i) {
+    const int pb = (w + kDelWaves * i) * 1024 + 16 * lane;
+    int off = 0;
+    if (pb < C::OFF_V) {
+      const int r = pb / DQK, c = (pb % DQK) / 16;
+      off = r * DQK + 16 * tile_slot<DQK>(r, c);
+    } else if (pb < C::OFF_KS) {
+      const int p = pb - C::OFF_V, r = p / DV, c = (p % DV) / 16;
+      off = r * DV + 16 * tile_slot<DV>(r, c);
+    } else if (pb < C::OFF_VS) {
+      off = pb - C::OFF_KS;
+    } else {
+      off = pb - C::OFF_VS;
+    }
+    soff[i] = off;
+  }
+  auto issue = [&](int cc, int buf) {         // chunk cc -> buffer buf
+#pragma unroll
+    for (int i = 0; i < C::NJW; ++i) {
+      const int j = w + kDelWaves * i;
+      if (j >= C::NJ) continue;
+      const int jb = j * 1024;
+      const uint8_t* base;
+      if (jb < C::OFF_V) base = Kc + (int64_t)cc * kChunk * DQK;
+      else if (jb < C::OFF_KS) base = Vc + (int64_t)cc * kChunk * DV;
+      else if (jb < C::OFF_VS) base = reinterpret_cast<const uint8_t*>(Kcs + (int64_t)cc * kChunk * KB);
+      else base = reinterpret_cast<const uint8_t*>(Vcs + (int64_t)cc * kChunk * VB);
+      dma16(base + soff[i], lds + buf * C::BUF + jb);
+    }
+  };
+
   v8i qb[KS], db[VS];
   int qsc[KS], dsc[VS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    const uint8_t* p = Qc + (int64_t)qi * DQK + 64 * ks;
-    qb[ks] = cat(*reinterpret_cast<const v4i*>(p + 16 * h), *reinterpret_cast<const v4i*>(p + 32 + 16 * h));
-    qsc[ks] = e8m0(Qcs[(int64_t)qi * KB + 2 * ks + h]);
+    if (live) {
+      const uint8_t* p = qc + (qhead * Lp + qi) * DQK + 64 * ks;
+      qb[ks] = cat(*reinterpret_cast<const v4i*>(p + 16 * h), *reinterpret_cast<const v4i*>(p + 32 + 16 * h));
+      qsc[ks] = e8m0(qcs[(qhead * Lp + qi) * KB + 2 * ks + h]);
+    } else {
+      qb[ks] = v8i{};
+      qsc[ks] = 127;
+    }
   }
 #pragma unroll
   for (int ks = 0; ks < VS; ++ks) {
-    const uint8_t* p = dOc + (int64_t)qi * DV + 64 * ks;
-    db[ks] = cat(*reinterpret_cast<const v4i*>(p + 16 * h), *reinterpret_cast<const v4i*>(p + 32 + 16 * h));
-    dsc[ks] = e8m0(dOcs[(int64_t)qi * VB + 2 * ks + h]);
+    if (live) {
+      const uint8_t* p = doc + (qhead * Lp + qi) * DV + 64 * ks;
+      db[ks] = cat(*reinterpret_cast<const v4i*>(p + 16 * h), *reinterpret_cast<const v4i*>(p + 32 + 16 * h));
+      dsc[ks] = e8m0(docs[(qhead * Lp + qi) * VB + 2 * ks + h]);
+    } else {
+      db[ks] = v8i{};
+      dsc[ks] = 127;
+    }
   }
+  const int kr = pair_row(R);
+  int kro[KS][2], vro[VS][2];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) kro[ks][e] = kr * DQK + 16 * tile_slot<DQK>(kr, 4 * ks + 2 * e + h);
+#pragma unroll
+  for (int ks = 0; ks < VS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) vro[ks][e] = kr * DV + 16 * tile_slot<DV>(kr, 4 * ks + 2 * e + h);
+
   const float c2 = sigma * kLog2e;
-  const float l2 = (qi < L) ? lse[qhead * L + qi] * kLog2e : 0.f;
+  const float l2 = (live && qi < L) ? lse[qhead * L + qi] * kLog2e : 0.f;
   double acc = 0.0;                              // FP32 per chunk, FP64 across chunks
-  const int nchunks = CAUSAL ? (qt + 1) : nqt;
-  const int krow_a = pair_row(R);
+  const int qlast = min(q0 + kDelQ, Lp) - 1;
+  const int nchunks = CAUSAL ? (qlast / kChunk + 1) : Lp / kChunk;
+  const int wlast = CAUSAL ? min(nchunks - 1, (qw + 31) / kChunk) : nchunks - 1;
+
+  // S^T and dP^T tiles of key tile t of the chunk in buffer buf
+  auto tiles = [&](int buf, int t, v16f& s, v16f& dp) {
+    const uint8_t* bb = lds + buf * C::BUF;
+    const float* ks_ = reinterpret_cast<const float*>(bb + C::OFF_KS) + (32 * t + kr) * KB;
+    const float* vs_ = reinterpret_cast<const float*>(bb + C::OFF_VS) + (32 * t + kr) * VB;
+    s = v16f{};
+    dp = v16f{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint8_t* p = bb + 32 * t * DQK;
+      const v8i a = cat(lds_read16(p + kro[ks][0]), lds_read16(p + kro[ks][1]));
+      s = mfma<E4M3, E4M3>(a, qb[ks], s, e8m0(ks_[2 * ks + h]), qsc[ks]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < VS; ++ks) {
+      const uint8_t* p = bb + C::OFF_V + 32 * t * DV;
+      const v8i a = cat(lds_read16(p + vro[ks][0]), lds_read16(p + vro[ks][1]));
+      dp = mfma<E4M3, E5M2>(a, db[ks], dp, e8m0(vs_[2 * ks + h]), dsc[ks]);
+    }
+  };
+
+  issue(0, 0);
+  if (nchunks > 1) issue(1, 1);
+  wait_vmem();
+  __syncthreads();
+  v16f s[4], dp[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if (live) tiles(0, t, s[t], dp[t]);
+    else s[t] = dp[t] = v16f{};
+  }
   for (int c = 0; c < nchunks; ++c) {
     const int k0 = c * kChunk;
-    __syncthreads();
-    for (int i = tid; i < kChunk * DQK / 16; i += 256) {
-      const int row = (i * 16) / DQK, col = (i * 16) % DQK;
-      *reinterpret_cast<v4i*>(sK + row * KROW + col) = *reinterpret_cast<const v4i*>(Kc + (int64_t)(k0 + row) * DQK + col);
-    }
-    for (int i = tid; i < kChunk * KB / 4; i += 256)
-      *reinterpret_cast<v4f*>(sKs + 4 * i) = *reinterpret_cast<const v4f*>(Kcs + (int64_t)k0 * KB + 4 * i);
-    for (int i = tid; i < kChunk * DV / 16; i += 256) {
-      const int row = (i * 16) / DV, col = (i * 16) % DV;
-      *reinterpret_cast<v4i*>(sV + row * VROW + col) = *reinterpret_cast<const v4i*>(Vc + (int64_t)(k0 + row) * DV + col);
-    }
-    for (int i = tid; i < kChunk * VB / 4; i += 256)
-      *reinterpret_cast<v4f*>(sVs + 4 * i) = *reinterpret_cast<const v4f*>(Vcs + (int64_t)k0 * VB + 4 * i);
-    __syncthreads();
-    if (CAUSAL && k0 > q0 + 32 * w + 31) continue;
-    const bool need_mask = (k0 + kChunk > L) || (CAUSAL && k0 + kChunk - 1 > q0 + 32 * w);
-    float cacc = 0.f;
+    wait_vmem();
+    __syncthreads();                             // chunk c+1 landed; buffer c%2 free
+    if (c + 2 < nchunks) issue(c + 2, c & 1);
+    if (!live || c > wlast) continue;
+    if ((k0 + kChunk > L) || (CAUSAL && k0 + kChunk - 1 > qw)) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int krow = 32 * t + krow_a;
-      v16f s = v16f{}, dp = v16f{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint8_t* p = sK + krow * KROW + 64 * ks;
-        v8i a = cat(lds_read16(p + 16 * h), lds_read16(p + 32 + 16 * h));
-        s = mfma<E4M3, E4M3>(a, qb[ks], s, e8m0(sKs[krow * KB + 2 * ks + h]), qsc[ks]);
-      }
-#pragma unroll
-      for (int ks = 0; ks < VS; ++ks) {
-        const uint8_t* p = sV + krow * VROW + 64 * ks;
-        v8i a = cat(lds_read16(p + 16 * h), lds_read16(p + 32 + 16 * h));
-        dp = mfma<E4M3, E5M2>(a, db[ks], dp, e8m0(sVs[krow * VB + 2 * ks + h]), dsc[ks]);
-      }
-      if (need_mask) {
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int kk = k0 + 32 * t + 16 * h + v;
-          if (kk >= L || (CAUSAL && kk > qi)) s[v] = -INFINITY;
+          if (kk >= L || (CAUSAL && kk > qi)) s[t][v] = -INFINITY;
         }
-      }
+    }
+    float cacc = 0.f;
+    const int nb = (c + 1) & 1;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[v], c2, -l2));
-        cacc = fmaf(p, dp[v], cacc);
-      }
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) cacc = fmaf(__builtin_amdgcn_exp2f(fmaf(s[t][v], c2, -l2)), dp[t][v], cacc);
+      // tile t of chunk c+1 (unused past this wave's last chunk)
+      tiles(nb, t, s[t], dp[t]);
     }
     acc += (double)cacc;
   }
+  if (!live) return;
   acc = pair_sum_d(acc);
   if (qi < L && h == 0) delta[qhead * L + qi] = (float)acc;
 }
@@ -193,13 +277,15 @@ __global__ __launch_bounds__(256, 2) void delta_matched_kernel(
 template <int DQK, int DV>
 static void launch_dm_t(const AttnDims& d, Operand doc, Operand q, Operand k, Operand v, const float* lse,
                         float* delta, hipStream_t s) {
-  dim3 grid(d.Lp / kChunk, d.Hq, d.B);
+  dim3 grid((unsigned)((d.Lp + kDelQ - 1) / kDelQ) * d.Hq * d.B);
   if (d.causal)
-    hipLaunchKernelGGL((delta_matched_kernel<DQK, DV, true>), grid, dim3(256), 0, s, q.codes, q.scales, k.codes,
-                       k.scales, v.codes, v.scales, doc.codes, doc.scales, lse, delta, d.Hq, d.Hkv, d.L, d.Lp, d.sigma);
+    hipLaunchKernelGGL((delta_matched_kernel<DQK, DV, true>), grid, dim3(64 * kDelWaves), 0, s, q.codes, q.scales,
+                       k.codes, k.scales, v.codes, v.scales, doc.codes, doc.scales, lse, delta, d.Hq, d.Hkv, d.L,
+                       d.Lp, d.sigma);
   else
-    hipLaunchKernelGGL((delta_matched_kernel<DQK, DV, false>), grid, dim3(256), 0, s, q.codes, q.scales, k.codes,
-                       k.scales, v.codes, v.scales, doc.codes, doc.scales, lse, delta, d.Hq, d.Hkv, d.L, d.Lp, d.sigma);
+    hipLaunchKernelGGL((delta_matched_kernel<DQK, DV, false>), grid, dim3(64 * kDelWaves), 0, s, q.codes, q.scales,
+                       k.codes, k.scales, v.codes, v.scales, doc.codes, doc.scales, lse, delta, d.Hq, d.Hkv, d.L,
+                       d.Lp, d.sigma);
 }
 
 hipError_t launch_delta_matched(const AttnDims& d, Operand doc, Operand q, Operand k, Operand v, const float* lse,

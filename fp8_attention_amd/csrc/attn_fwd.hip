@@ -1,7 +1,8 @@
 // Forward of block-scaled FP8 attention on gfx950 matrix cores.
 //
-// Workgroup = 8 waves = 256 queries (32 per wave, 2 waves per SIMD); grid =
-// (query tiles of 256, Hq, B).  Each wave keeps its queries' Q^<c> codes in
+// Workgroup = 8 waves = 256 queries (32 per wave, 2 waves per SIMD); a 1-D grid
+// over (query tile of 256, Hq, B) with the query tile slowest, so the longest
+// causal tiles are dispatched first.  Each wave keeps its queries' Q^<c> codes in
 // registers as the B operand of S^T = K Q^T, so the score tile comes out with
 // one query per lane pair (R, R+32) and 16 keys per lane -- exactly the
 // B-operand layout the P V product needs, so the probabilities are cast to E4M3
@@ -61,8 +62,10 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_kernel(
   const int lane = tid & 63, w = tid >> 6;
   const int R = lane & 31, h = lane >> 5;
   const int nqt = (Lp + kFwdQ - 1) / kFwdQ;
-  const int qt = CAUSAL ? (nqt - 1 - (int)blockIdx.x) : (int)blockIdx.x;
-  const int hq = blockIdx.y, b = blockIdx.z;
+  const int nhb = Hq * (int)(gridDim.x / (nqt * Hq));      // Hq * B
+  const int tr = (int)blockIdx.x / nhb, hb = (int)blockIdx.x % nhb;
+  const int qt = CAUSAL ? (nqt - 1 - tr) : tr;            // longest causal tiles dispatched first
+  const int hq = hb % Hq, b = hb / Hq;
   const int hk = hq / (Hq / Hkv);
   const int q0 = qt * kFwdQ;
   const int qw = q0 + 32 * w;                 // first query of this wave
@@ -264,7 +267,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_kernel(
 
 template <int DQK, int DV>
 static void launch_fwd_t(const AttnDims& d, Operand q, Operand k, Operand v, float* o, float* lse, hipStream_t s) {
-  dim3 grid((d.Lp + kFwdQ - 1) / kFwdQ, d.Hq, d.B);
+  dim3 grid((unsigned)((d.Lp + kFwdQ - 1) / kFwdQ) * d.Hq * d.B);
   if (d.causal)
     hipLaunchKernelGGL((fwd_kernel<DQK, DV, true>), grid, dim3(64 * kFwdWaves), 0, s, q.codes, q.scales, k.codes,
                        k.scales, v.codes, v.scales, o, lse, d.Hq, d.Hkv, d.L, d.Lp, d.sigma);
