@@ -22,6 +22,9 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 # Attention kernels: scores are finite or -inf by construction, so max
 # reductions need no NaN canonicalisation (this lets them map onto v_max3_f32).
 EXTRA = {src: ["-fno-honor-nans"] for src in ("attn_fwd.hip", "attn_delta.hip", "attn_bwd.hip", "attn_dq.hip")}
+# dK/dV runs one wave per SIMD with its accumulators in AGPRs; keep the score tiles'
+# MFMA results in VGPRs so the FP32 softmax work does not shuttle them through AGPRs.
+EXTRA["attn_bwd.hip"] += ["-mllvm", "--amdgpu-mfma-vgpr-form"]
 
 
 def _compile(src: str) -> str:

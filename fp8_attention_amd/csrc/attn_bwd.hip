@@ -291,7 +291,6 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
         }
         pscl[j] = kp + 127;
         dscl[j] = kd + 127;
-        __builtin_amdgcn_sched_barrier(0);          // bound the live operand tiles (register budget)
       }
 
       // dV^T += dO^<s>^T P^<q>, dK^T += Q^<s>^T dS^<q> over the step's 64 queries.
