@@ -1,0 +1,12 @@
+// dQ for d_qk = 192, d_v = 128 in a translation unit of its own (see build.py).
+#include "attn_dq.h"
+
+namespace dm {
+
+hipError_t launch_dq_192_128(const AttnDims& d, Operand qc, Operand kc, Operand ks, Operand vc, Operand doc,
+                             const float* lse, const float* delta, float* dq, double* ps, double* pa, hipStream_t s) {
+  launch_dq_t<192, 128>(d, qc, kc, ks, vc, doc, lse, delta, dq, ps, pa, s);
+  return hipGetLastError();
+}
+
+}  // namespace dm
