@@ -1,22 +1,26 @@
 // dK and dV of block-scaled FP8 attention (key-stationary).
 //
-// Workgroup = NW waves, wave w owning keys k0+32w .. k0+32w+31 and every channel;
-// a 1-D grid over (key tile, Hkv, B) with key tiles slowest, so the long causal
-// tiles start first.  The workgroup walks the query heads of its KV group and, for each, the
-// 64-query steps that can see its keys.  Per step and wave:
-//   S^T = Q K^T and dP^T = dO V^T for two 32-query tiles (scaled FP8 MFMA; one key
-//   per lane pair, 16 queries per lane); P = exp(S - LSE), dS = P (dP^ - delta)
-//   in FP32; the 32-query block casts P^<q> (E4M3) and dS^<q> (E5M2) happen in
-//   registers, and the two tiles' codes side by side are exactly the B operands
-//   of dV^T += dO^<s>^T P^<q> and dK^T += Q^<s>^T dS^<q> (64 queries per product),
-//   so nothing is exchanged between waves.
+// Workgroup = 8 waves over 128 keys: key group kg = w % 4 owns keys
+// k0+32kg .. k0+32kg+31, and the two waves of a key group split the outputs --
+// role 0 accumulates dV, role 1 accumulates dK -- so each wave carries one set
+// of accumulators and two waves share every SIMD.  A 1-D grid over (key tile,
+// Hkv, B) with key tiles slowest starts the long causal tiles first.  The
+// workgroup walks the query heads of its KV group and, for each, the 64-query
+// steps that can see its keys.  Per step, for two 32-query tiles:
+//   dV waves: S^T = Q K^T, P = exp(S - LSE), P^<q> (E4M3, 32-query blocks);
+//   dK waves: S^T, dP^T = dO V^T, dS = P (dP^ - delta), dS^<q> (E5M2);
+// (one key per lane pair, 16 queries per lane), and the two tiles' codes side by
+// side are exactly the B operands of dV^T += dO^<s>^T P^<q> and
+// dK^T += Q^<s>^T dS^<q> over the step's 64 queries -- nothing passes between
+// waves.  S is recomputed by both waves of a key group: 25% more matrix work
+// for half the accumulator registers.
 // K^<c>/V^<c> of the workgroup's keys sit in LDS for the whole kernel; the
 // query-side tiles of step i+1 (Q^<c>, dO^<c> rows, Q^<s>, dO^<s> channel rows,
 // their scales) arrive in a second LDS buffer by direct global->LDS loads issued
 // during step i, with LSE and delta through registers; one barrier per step.  dK
 // and dV accumulate in registers over every query head of the group and are
 // written once (no atomics).  dQ is computed by the query-stationary kernel in
-// attn_dq.hip.
+// attn_dq.h.
 #include "dm_common.h"
 #include "dm_internal.h"
 
@@ -26,9 +30,10 @@ constexpr int kBQ = 64;          // queries per step
 
 template <int DQK, int DV>
 struct DkdvCfg {
-  static constexpr int NW = 4;                           // waves (32 keys each), one per SIMD
+  static constexpr int NKG = 4;                          // key groups of 32 keys
+  static constexpr int NW = 2 * NKG;                     // a dV wave and a dK wave per key group
   static constexpr int NT = 64 * NW;
-  static constexpr int KT = 32 * NW;                     // keys per workgroup
+  static constexpr int KT = 32 * NKG;                    // keys per workgroup
   static constexpr int KB = DQK / 32, VB = DV / 32;
   static constexpr int pad1k(int x) { return (x + 1023) / 1024 * 1024; }
   // resident K/V tile
@@ -65,6 +70,7 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
   using C = DkdvCfg<DQK, DV>;
   constexpr int NW = C::NW, NT = C::NT, KT = C::KT, KB = C::KB, VB = C::VB;
   constexpr int KS = DQK / 64, VS = DV / 64, NKT = DQK / 32, NVT = DV / 32;
+  constexpr int NACC = NKT > NVT ? NKT : NVT;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::BYTES];
   uint8_t* const stage0 = lds + C::KV_BYTES;
 
@@ -76,7 +82,8 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
   const int hk = (int)blockIdx.x % nhb % Hkv, b = (int)blockIdx.x % nhb / Hkv;
   const int k0 = ((int)blockIdx.x / nhb) * KT;            // key tiles slowest: long causal tiles first
   const int G = Hq / Hkv;
-  const int kw0 = k0 + 32 * w;                       // this wave's first key
+  const int kg = w & (C::NKG - 1), role = w / C::NKG;   // role 0: dV, role 1: dK
+  const int kw0 = k0 + 32 * kg;                      // this wave's first key
   const int key = kw0 + R;                           // this lane's key (column of the S^T tiles)
   const int LB = Lp / kBlock;
   const int64_t khead = (int64_t)b * Hkv + hk;
@@ -174,11 +181,9 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
     }
   };
 
-  v16f dkacc[NKT], dvacc[NVT];
+  v16f acc[NACC];                                    // dV^T (role 0) or dK^T (role 1) channel tiles
 #pragma unroll
-  for (int i = 0; i < NKT; ++i) dkacc[i] = v16f{};
-#pragma unroll
-  for (int i = 0; i < NVT; ++i) dvacc[i] = v16f{};
+  for (int i = 0; i < NACC; ++i) acc[i] = v16f{};
 
   const float c2 = sigma * kLog2e;
   const int qstart = CAUSAL ? k0 : 0;
@@ -195,14 +200,14 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       oq[ks][e] = prow * DQK + 16 * tile_slot<DQK>(prow, 4 * ks + 2 * e + h);
-      ok[ks][e] = (32 * w + R) * DQK + 16 * tile_slot<DQK>(R, 4 * ks + 2 * e + h);
+      ok[ks][e] = (32 * kg + R) * DQK + 16 * tile_slot<DQK>(R, 4 * ks + 2 * e + h);
     }
 #pragma unroll
   for (int ks = 0; ks < VS; ++ks)
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       od[ks][e] = prow * DV + 16 * tile_slot<DV>(prow, 4 * ks + 2 * e + h);
-      ov[ks][e] = (32 * w + R) * DV + 16 * tile_slot<DV>(R, 4 * ks + 2 * e + h);
+      ov[ks][e] = (32 * kg + R) * DV + 16 * tile_slot<DV>(R, 4 * ks + 2 * e + h);
     }
 #pragma unroll
   for (int e = 0; e < 2; ++e) ot[e] = R * kBQ + 16 * tile_slot<64>(R, 2 * e + h);
@@ -230,17 +235,15 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
     if (kw0 < L && (!CAUSAL || q0 + kBQ - 1 >= kw0)) {
       const bool need_mask = (kw0 + 32 > L) || (CAUSAL && q0 < kw0 + 31);
       // this wave's K and V rows are the B operands (lane R = key, K-slots = channels)
-      const float* ksr = reinterpret_cast<const float*>(lds + C::KS_OFF) + (32 * w + R) * KB;
-      const float* vsr = reinterpret_cast<const float*>(lds + C::VS_OFF) + (32 * w + R) * VB;
-      v4i pcode[2], dcode[2];
-      int pscl[2], dscl[2];
+      const float* ksr = reinterpret_cast<const float*>(lds + C::KS_OFF) + (32 * kg + R) * KB;
+      const float* vsr = reinterpret_cast<const float*>(lds + C::VS_OFF) + (32 * kg + R) * VB;
+      v4i code[2];
+      int scl[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        // S^T and dP^T for queries 32j .. 32j+31 of the step (rows in pair_row order)
+        // S^T (and dP^T) for queries 32j .. 32j+31 of the step (rows in pair_row order)
         const uint8_t* qt = st + C::QC + 32 * j * DQK;
-        const uint8_t* dt = st + C::DOC + 32 * j * DV;
         const float* qsr = reinterpret_cast<const float*>(st + C::QCS) + (32 * j + R) * KB;
-        const float* dsr = reinterpret_cast<const float*>(st + C::DOCS) + (32 * j + R) * VB;
         v16f s = v16f{}, dp = v16f{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -248,11 +251,15 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
           const v8i bk = cat(lds_read16(lds + C::K_OFF + ok[ks][0]), lds_read16(lds + C::K_OFF + ok[ks][1]));
           s = mfma<E4M3, E4M3>(a, bk, s, e8m0(qsr[2 * ks + h]), e8m0(ksr[2 * ks + h]));
         }
+        if (role) {
+          const uint8_t* dt = st + C::DOC + 32 * j * DV;
+          const float* dsr = reinterpret_cast<const float*>(st + C::DOCS) + (32 * j + R) * VB;
 #pragma unroll
-        for (int ks = 0; ks < VS; ++ks) {
-          const v8i a = cat(lds_read16(dt + od[ks][0]), lds_read16(dt + od[ks][1]));
-          const v8i bv = cat(lds_read16(lds + C::V_OFF + ov[ks][0]), lds_read16(lds + C::V_OFF + ov[ks][1]));
-          dp = mfma<E5M2, E4M3>(a, bv, dp, e8m0(dsr[2 * ks + h]), e8m0(vsr[2 * ks + h]));
+          for (int ks = 0; ks < VS; ++ks) {
+            const v8i a = cat(lds_read16(dt + od[ks][0]), lds_read16(dt + od[ks][1]));
+            const v8i bv = cat(lds_read16(lds + C::V_OFF + ov[ks][0]), lds_read16(lds + C::V_OFF + ov[ks][1]));
+            dp = mfma<E5M2, E4M3>(a, bv, dp, e8m0(dsr[2 * ks + h]), e8m0(vsr[2 * ks + h]));
+          }
         }
         // lane (key R, h), register v <-> step query 32j + 16h + v
         const float* l2p = reinterpret_cast<const float*>(st + C::LSE) + 32 * j + 16 * h;
@@ -264,56 +271,70 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
             if (key >= L || (CAUSAL && key > q)) s[v] = -INFINITY;
           }
         }
-        float am = 0.f, dm = 0.f;
+        float am = 0.f;
+        if (!role) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const v4f l4 = *reinterpret_cast<const v4f*>(l2p + 4 * g);
-          const v4f d4 = *reinterpret_cast<const v4f*>(dlp + 4 * g);
+          for (int g = 0; g < 4; ++g) {
+            const v4f l4 = *reinterpret_cast<const v4f*>(l2p + 4 * g);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int v = 4 * g + e;
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[v], c2, -l4[e]));
-            const float d = p * (dp[v] - d4[e]);
-            s[v] = p;                                 // s now holds P
-            dp[v] = d;                                // dp now holds dS
-            am = fmaxf(am, p);
-            dm = fmaxf(dm, fabsf(d));
+            for (int e = 0; e < 4; ++e) {
+              const float p = __builtin_amdgcn_exp2f(fmaf(s[4 * g + e], c2, -l4[e]));
+              s[4 * g + e] = p;                     // s now holds P
+              am = fmaxf(am, p);
+            }
           }
-        }
-        am = pair_max(am);
-        dm = pair_max(dm);
-        const int kp = scale_exp<E4M3>(am), kd = scale_exp<E5M2>(dm);
-        const float sp = exp2i(kp), sd = exp2i(kd);
+          am = pair_max(am);
+          const int k = scale_exp<E4M3>(am);
+          const float sc = exp2i(k);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          pcode[j][g] = (int)pack4s<E4M3>(s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3], sp);
-          dcode[j][g] = (int)pack4s<E5M2>(dp[4 * g], dp[4 * g + 1], dp[4 * g + 2], dp[4 * g + 3], sd);
+          for (int g = 0; g < 4; ++g) code[j][g] = (int)pack4s<E4M3>(s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3], sc);
+          scl[j] = k + 127;
+        } else {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const v4f l4 = *reinterpret_cast<const v4f*>(l2p + 4 * g);
+            const v4f d4 = *reinterpret_cast<const v4f*>(dlp + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int v = 4 * g + e;
+              const float p = __builtin_amdgcn_exp2f(fmaf(s[v], c2, -l4[e]));
+              const float d = p * (dp[v] - d4[e]);
+              dp[v] = d;                            // dp now holds dS
+              am = fmaxf(am, fabsf(d));
+            }
+          }
+          am = pair_max(am);
+          const int k = scale_exp<E5M2>(am);
+          const float sc = exp2i(k);
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            code[j][g] = (int)pack4s<E5M2>(dp[4 * g], dp[4 * g + 1], dp[4 * g + 2], dp[4 * g + 3], sc);
+          scl[j] = k + 127;
         }
-        pscl[j] = kp + 127;
-        dscl[j] = kd + 127;
       }
 
-      // dV^T += dO^<s>^T P^<q>, dK^T += Q^<s>^T dS^<q> over the step's 64 queries.
-      // B operand: lane (key R, h) holds queries 16h.. of tile 0 and of tile 1.
-      const v8i pq = cat(pcode[0], pcode[1]);
-      const v8i dsq = cat(dcode[0], dcode[1]);
-      const int psc = h ? pscl[1] : pscl[0];
-      const int dsc = h ? dscl[1] : dscl[0];
-      const float* qssr = reinterpret_cast<const float*>(st + C::QSS);
-      const float* dossr = reinterpret_cast<const float*>(st + C::DOSS);
+      // dV^T += dO^<s>^T P^<q> (role 0) or dK^T += Q^<s>^T dS^<q> (role 1) over the step's 64
+      // queries.  B operand: lane (key R, h) holds queries 16h.. of tile 0 and of tile 1.
+      const v8i bq = cat(code[0], code[1]);
+      const int bsc = h ? scl[1] : scl[0];
+      if (!role) {
+        const float* dossr = reinterpret_cast<const float*>(st + C::DOSS);
 #pragma unroll
-      for (int ct = 0; ct < NVT; ++ct) {
-        const int ch = 32 * ct + R;
-        const uint8_t* p = st + C::DOS + 32 * ct * kBQ;
-        const v8i a = cat(lds_read16(p + ot[0]), lds_read16(p + ot[1]));
-        dvacc[ct] = mfma<E5M2, E4M3>(a, pq, dvacc[ct], e8m0(dossr[2 * ch + h]), psc);
-      }
+        for (int ct = 0; ct < NVT; ++ct) {
+          const int ch = 32 * ct + R;
+          const uint8_t* p = st + C::DOS + 32 * ct * kBQ;
+          const v8i a = cat(lds_read16(p + ot[0]), lds_read16(p + ot[1]));
+          acc[ct] = mfma<E5M2, E4M3>(a, bq, acc[ct], e8m0(dossr[2 * ch + h]), bsc);
+        }
+      } else {
+        const float* qssr = reinterpret_cast<const float*>(st + C::QSS);
 #pragma unroll
-      for (int ct = 0; ct < NKT; ++ct) {
-        const int ch = 32 * ct + R;
-        const uint8_t* p = st + C::QS + 32 * ct * kBQ;
-        const v8i a = cat(lds_read16(p + ot[0]), lds_read16(p + ot[1]));
-        dkacc[ct] = mfma<E4M3, E5M2>(a, dsq, dkacc[ct], e8m0(qssr[2 * ch + h]), dsc);
+        for (int ct = 0; ct < NKT; ++ct) {
+          const int ch = 32 * ct + R;
+          const uint8_t* p = st + C::QS + 32 * ct * kBQ;
+          const v8i a = cat(lds_read16(p + ot[0]), lds_read16(p + ot[1]));
+          acc[ct] = mfma<E4M3, E5M2>(a, bq, acc[ct], e8m0(qssr[2 * ch + h]), bsc);
+        }
       }
     }
     if (more) store_small(stn);
@@ -321,23 +342,26 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
 
   // ---- dK, dV written once per key: register v of channel tile ct <-> channel 32ct + 8(v/4) + 4h + v%4
   if (key < L) {
-    float* dkr = dk + (khead * L + key) * DQK + 4 * h;
-    float* dvr = dv + (khead * L + key) * DV + 4 * h;
+    if (role) {
+      float* dkr = dk + (khead * L + key) * DQK + 4 * h;
 #pragma unroll
-    for (int ct = 0; ct < NKT; ++ct)
+      for (int ct = 0; ct < NKT; ++ct)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        v4f r = {sigma * dkacc[ct][4 * a], sigma * dkacc[ct][4 * a + 1], sigma * dkacc[ct][4 * a + 2],
-                 sigma * dkacc[ct][4 * a + 3]};
-        *reinterpret_cast<v4f*>(dkr + 32 * ct + 8 * a) = r;
-      }
+        for (int a = 0; a < 4; ++a) {
+          v4f r = {sigma * acc[ct][4 * a], sigma * acc[ct][4 * a + 1], sigma * acc[ct][4 * a + 2],
+                   sigma * acc[ct][4 * a + 3]};
+          *reinterpret_cast<v4f*>(dkr + 32 * ct + 8 * a) = r;
+        }
+    } else {
+      float* dvr = dv + (khead * L + key) * DV + 4 * h;
 #pragma unroll
-    for (int ct = 0; ct < NVT; ++ct)
+      for (int ct = 0; ct < NVT; ++ct)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        v4f r = {dvacc[ct][4 * a], dvacc[ct][4 * a + 1], dvacc[ct][4 * a + 2], dvacc[ct][4 * a + 3]};
-        *reinterpret_cast<v4f*>(dvr + 32 * ct + 8 * a) = r;
-      }
+        for (int a = 0; a < 4; ++a) {
+          v4f r = {acc[ct][4 * a], acc[ct][4 * a + 1], acc[ct][4 * a + 2], acc[ct][4 * a + 3]};
+          *reinterpret_cast<v4f*>(dvr + 32 * ct + 8 * a) = r;
+        }
+    }
   }
 }
 
