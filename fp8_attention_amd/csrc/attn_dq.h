@@ -1,7 +1,8 @@
 // dQ of block-scaled FP8 attention (query-stationary), with the row-sum probes.
 //
-// Workgroup = 8 waves = 256 queries (32 per wave); a 1-D grid over (query tile,
-// Hq, B) with the query tile slowest, so the longest causal tiles start first.
+// Workgroup = 8 waves = 256 queries (32 per wave; 4 waves when the probes are on);
+// a 1-D grid over (query tile, Hq, B) with the query tile slowest, so the longest
+// causal tiles start first.
 // The wave's Q^<c> and dO^<c> rows sit in registers as the B operands of
 // S^T = K Q^T and dP^T = V dO^T, so both score tiles come out with one query per
 // lane pair and 16 keys per lane.  Per 128-key chunk and 32-key tile:
@@ -13,15 +14,18 @@
 // K^<c>, V^<c> and K^<s> chunks arrive in double-buffered LDS by direct
 // global->LDS loads issued one chunk ahead; one barrier per chunk.
 #pragma once
+#include <type_traits>
+
 #include "dm_common.h"
 #include "dm_internal.h"
 
 namespace dm {
 
-constexpr int kDqWaves = 4;
-constexpr int kDqQ = 32 * kDqWaves;
+// waves per workgroup (32 queries each): 8 (two per SIMD); the probe variant, with
+// its extra row sums live, runs one wave per SIMD with the full register file
+template <bool PROBE> constexpr int dq_waves() { return PROBE ? 4 : 8; }
 
-template <int DQK, int DV>
+template <int DQK, int DV, int NW>
 struct DqLds {
   static constexpr int KB = DQK / 32, VB = DV / 32;
   // K part: K^<c> rows [128][DQK] (swizzled) + scales [128][KB]
@@ -32,20 +36,21 @@ struct DqLds {
   static constexpr int OFF_VP = 2 * KPART;                      // V parts follow the two K parts
   static constexpr int BYTES = 2 * KPART + 2 * VPART;
   static constexpr int NJK = KPART / 1024, NJV = VPART / 1024;
-  static constexpr int NJKW = (NJK + kDqWaves - 1) / kDqWaves, NJVW = (NJV + kDqWaves - 1) / kDqWaves;
+  static constexpr int NJKW = (NJK + NW - 1) / NW, NJVW = (NJV + NW - 1) / NW;
   static_assert(K % 1024 == 0 && KS % 1024 == 0 && V % 1024 == 0 && VS % 1024 == 0 && T % 1024 == 0 &&
                 TS % 1024 == 0, "whole 1 KB loads");
 };
 
 template <int DQK, int DV, bool CAUSAL, bool PROBE>
-__global__ __launch_bounds__(64 * kDqWaves) void dq_kernel(
+__global__ __launch_bounds__(64 * dq_waves<PROBE>()) void dq_kernel(
     const uint8_t* __restrict__ qc, const float* __restrict__ qcs, const uint8_t* __restrict__ kc,
     const float* __restrict__ kcs, const uint8_t* __restrict__ vc, const float* __restrict__ vcs,
     const uint8_t* __restrict__ kst, const float* __restrict__ ksts, const uint8_t* __restrict__ doc,
     const float* __restrict__ docs, const float* __restrict__ lse, const float* __restrict__ delta,
     float* __restrict__ dq, double* __restrict__ psum, double* __restrict__ pabs, int Hq, int Hkv, int L, int Lp,
     float sigma) {
-  using C = DqLds<DQK, DV>;
+  constexpr int kDqWaves = dq_waves<PROBE>(), kDqQ = 32 * kDqWaves;
+  using C = DqLds<DQK, DV, kDqWaves>;
   constexpr int KS = DQK / 64, VS = DV / 64, KB = DQK / 32, VB = DV / 32;
   constexpr int NCT = DQK / 32;                 // 32-channel tiles of dQ^T
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::BYTES];
@@ -192,18 +197,10 @@ __global__ __launch_bounds__(64 * kDqWaves) void dq_kernel(
     return a_;
   };
 
-  issue_k(0, 0);
-  issue_v(0, 0);
-  for (int c = 0; c < nchunks; ++c) {
+  // one chunk of work for this wave; MASK instantiates the causal / ragged mask
+  auto chunk = [&](int c, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int k0 = c * kChunk;
-    wait_vmem();
-    __syncthreads();                             // chunk c landed; the other buffers are free
-    if (c + 1 < nchunks) {
-      issue_k(c + 1, (c + 1) & 1);
-      issue_v(c + 1, (c + 1) & 1);
-    }
-    if (!live || c > wlast) continue;
-    const bool need_mask = (k0 + kChunk > L) || (CAUSAL && k0 + kChunk - 1 > qw);
     const uint8_t* vp = lds + C::OFF_VP + (c & 1) * C::VPART;
     const float* tsp = reinterpret_cast<const float*>(vp + C::OFF_TS);
     v8i dsb[2];
@@ -221,7 +218,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void dq_kernel(
         dp = mfma<E4M3, E5M2>(a, db[ks], dp, e8m0(vsr[2 * ks + h]), dsc[ks]);
       }
       v16f sc_ = score_tile(c & 1, t);
-      if (need_mask) {
+      if constexpr (MASK) {
         // key k0 + 32t + 16h + v is visible iff it is <= kmax, i.e. iff v <= lim
         const int lim = kmax - (k0 + 32 * t + 16 * h);
 #pragma unroll
@@ -263,6 +260,30 @@ __global__ __launch_bounds__(64 * kDqWaves) void dq_kernel(
       rsum += (double)csum;
       rabs += (double)cabs;
     }
+  };
+  auto sync_and_issue = [&](int c) {
+    wait_vmem();
+    __syncthreads();                             // chunk c landed; the other buffers are free
+    if (c + 1 < nchunks) {
+      issue_k(c + 1, (c + 1) & 1);
+      issue_v(c + 1, (c + 1) & 1);
+    }
+  };
+
+  // Chunks before nfull need no mask for any wave of the workgroup (all their keys
+  // precede every query of the tile and lie below L); the rest take the masked body.
+  // Two loops keep the mask code out of the main loop's register allocation.
+  const int nfull = min(CAUSAL ? q0 / kChunk : nchunks, L / kChunk);
+  issue_k(0, 0);
+  issue_v(0, 0);
+  int c = 0;
+  for (; c < nfull; ++c) {
+    sync_and_issue(c);
+    if (live) chunk(c, std::false_type{});
+  }
+  for (; c < nchunks; ++c) {
+    sync_and_issue(c);
+    if (live && c <= wlast) chunk(c, std::true_type{});
   }
 
   if (!live) return;
@@ -292,8 +313,9 @@ __global__ __launch_bounds__(64 * kDqWaves) void dq_kernel(
 template <int DQK, int DV, bool CAUSAL, bool PROBE>
 static void launch_dq_t4(const AttnDims& d, Operand qc, Operand kc, Operand ks, Operand vc, Operand doc,
                          const float* lse, const float* delta, float* dq, double* ps, double* pa, hipStream_t s) {
+  constexpr int kDqQ = 32 * dq_waves<PROBE>();
   dim3 grid((unsigned)((d.Lp + kDqQ - 1) / kDqQ) * d.Hq * d.B);
-  hipLaunchKernelGGL((dq_kernel<DQK, DV, CAUSAL, PROBE>), grid, dim3(64 * kDqWaves), 0, s, qc.codes, qc.scales, kc.codes,
+  hipLaunchKernelGGL((dq_kernel<DQK, DV, CAUSAL, PROBE>), grid, dim3(2 * kDqQ), 0, s, qc.codes, qc.scales, kc.codes,
                      kc.scales, vc.codes, vc.scales, ks.codes, ks.scales, doc.codes, doc.scales, lse, delta, dq, ps,
                      pa, d.Hq, d.Hkv, d.L, d.Lp, d.sigma);
 }
