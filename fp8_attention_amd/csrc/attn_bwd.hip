@@ -21,6 +21,8 @@
 // and dV accumulate in registers over every query head of the group and are
 // written once (no atomics).  dQ is computed by the query-stationary kernel in
 // attn_dq.h.
+#include <type_traits>
+
 #include "dm_common.h"
 #include "dm_internal.h"
 
@@ -217,7 +219,9 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
     load_small(qhead0, qstart);
     store_small(stage0);
   }
-  for (int it = 0; it < total; ++it) {
+  // one step; MASK instantiates the causal / padded-key mask (kept out of the main loop)
+  auto step = [&](int it, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int hh = it / nsteps;
     const int q0 = qstart + (it - hh * nsteps) * kBQ;
     uint8_t* const st = stage0 + (it & 1) * C::STAGE;
@@ -233,7 +237,7 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
     }
 
     if (kw0 < L && (!CAUSAL || q0 + kBQ - 1 >= kw0)) {
-      const bool need_mask = (kw0 + 32 > L) || (CAUSAL && q0 < kw0 + 31);
+      const bool need_mask = MASK && ((kw0 + 32 > L) || (CAUSAL && q0 < kw0 + 31));
       // this wave's K and V rows are the B operands (lane R = key, K-slots = channels)
       const float* ksr = reinterpret_cast<const float*>(lds + C::KS_OFF) + (32 * kg + R) * KB;
       const float* vsr = reinterpret_cast<const float*>(lds + C::VS_OFF) + (32 * kg + R) * VB;
@@ -338,6 +342,13 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
       }
     }
     if (more) store_small(stn);
+  };
+  // per head: the steps that can need a mask (the first KT/kBQ for causal, all when the
+  // tile holds padded keys), then the rest in a loop without mask code
+  const int nmask = (k0 + KT > L) ? nsteps : (CAUSAL ? min(nsteps, KT / kBQ) : 0);
+  for (int hh = 0, it = 0; hh < G; ++hh) {
+    for (int i = 0; i < nmask; ++i, ++it) step(it, std::true_type{});
+    for (int i = nmask; i < nsteps; ++i, ++it) step(it, std::false_type{});
   }
 
   // ---- dK, dV written once per key: register v of channel tile ct <-> channel 32ct + 8(v/4) + 4h + v%4
