@@ -183,6 +183,10 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
     }
   };
 
+  // The two roles run role-specialised copies of the step loop (wave-uniform choice), so
+  // neither carries the other's code; both execute the same barriers.
+  auto run = [&](auto role_tag) {
+  constexpr bool DK = decltype(role_tag)::value;
   v16f acc[NACC];                                    // dV^T (role 0) or dK^T (role 1) channel tiles
 #pragma unroll
   for (int i = 0; i < NACC; ++i) acc[i] = v16f{};
@@ -255,7 +259,7 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
           const v8i bk = cat(lds_read16(lds + C::K_OFF + ok[ks][0]), lds_read16(lds + C::K_OFF + ok[ks][1]));
           s = mfma<E4M3, E4M3>(a, bk, s, e8m0(qsr[2 * ks + h]), e8m0(ksr[2 * ks + h]));
         }
-        if (role) {
+        if constexpr (DK) {
           const uint8_t* dt = st + C::DOC + 32 * j * DV;
           const float* dsr = reinterpret_cast<const float*>(st + C::DOCS) + (32 * j + R) * VB;
 #pragma unroll
@@ -276,7 +280,7 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
           }
         }
         float am = 0.f;
-        if (!role) {
+        if constexpr (!DK) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const v4f l4 = *reinterpret_cast<const v4f*>(l2p + 4 * g);
@@ -321,7 +325,7 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
       // queries.  B operand: lane (key R, h) holds queries 16h.. of tile 0 and of tile 1.
       const v8i bq = cat(code[0], code[1]);
       const int bsc = h ? scl[1] : scl[0];
-      if (!role) {
+      if constexpr (!DK) {
         const float* dossr = reinterpret_cast<const float*>(st + C::DOSS);
 #pragma unroll
         for (int ct = 0; ct < NVT; ++ct) {
@@ -353,7 +357,7 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
 
   // ---- dK, dV written once per key: register v of channel tile ct <-> channel 32ct + 8(v/4) + 4h + v%4
   if (key < L) {
-    if (role) {
+    if constexpr (DK) {
       float* dkr = dk + (khead * L + key) * DQK + 4 * h;
 #pragma unroll
       for (int ct = 0; ct < NKT; ++ct)
@@ -374,6 +378,9 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
         }
     }
   }
+  };
+  if (role) run(std::true_type{});
+  else run(std::false_type{});
 }
 
 template <int DQK, int DV>
