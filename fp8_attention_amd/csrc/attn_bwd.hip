@@ -223,6 +223,30 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
     load_small(qhead0, qstart);
     store_small(stage0);
   }
+  // this wave's K^<c> (and for dK, V^<c>) rows as register-resident B operands
+  // (lane R = key, K-slots = channels), read once after the resident tile is written
+  __syncthreads();
+  v8i kb[KS], vb[VS];
+  int ksc[KS], vsc[VS];
+  {
+    const float* ksr = reinterpret_cast<const float*>(lds + C::KS_OFF) + (32 * kg + R) * KB;
+    const float* vsr = reinterpret_cast<const float*>(lds + C::VS_OFF) + (32 * kg + R) * VB;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kb[ks] = cat(lds_read16(lds + C::K_OFF + ok[ks][0]), lds_read16(lds + C::K_OFF + ok[ks][1]));
+      ksc[ks] = e8m0(ksr[2 * ks + h]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < VS; ++ks) {
+      if constexpr (DK) {
+        vb[ks] = cat(lds_read16(lds + C::V_OFF + ov[ks][0]), lds_read16(lds + C::V_OFF + ov[ks][1]));
+        vsc[ks] = e8m0(vsr[2 * ks + h]);
+      } else {
+        vb[ks] = v8i{};
+        vsc[ks] = 127;
+      }
+    }
+  }
   // one step; MASK instantiates the causal / padded-key mask (kept out of the main loop)
   auto step = [&](int it, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
@@ -242,9 +266,6 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
 
     if (kw0 < L && (!CAUSAL || q0 + kBQ - 1 >= kw0)) {
       const bool need_mask = MASK && ((kw0 + 32 > L) || (CAUSAL && q0 < kw0 + 31));
-      // this wave's K and V rows are the B operands (lane R = key, K-slots = channels)
-      const float* ksr = reinterpret_cast<const float*>(lds + C::KS_OFF) + (32 * kg + R) * KB;
-      const float* vsr = reinterpret_cast<const float*>(lds + C::VS_OFF) + (32 * kg + R) * VB;
       v4i code[2];
       int scl[2];
 #pragma unroll
@@ -256,8 +277,7 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const v8i a = cat(lds_read16(qt + oq[ks][0]), lds_read16(qt + oq[ks][1]));
-          const v8i bk = cat(lds_read16(lds + C::K_OFF + ok[ks][0]), lds_read16(lds + C::K_OFF + ok[ks][1]));
-          s = mfma<E4M3, E4M3>(a, bk, s, e8m0(qsr[2 * ks + h]), e8m0(ksr[2 * ks + h]));
+          s = mfma<E4M3, E4M3>(a, kb[ks], s, e8m0(qsr[2 * ks + h]), ksc[ks]);
         }
         if constexpr (DK) {
           const uint8_t* dt = st + C::DOC + 32 * j * DV;
@@ -265,8 +285,7 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
 #pragma unroll
           for (int ks = 0; ks < VS; ++ks) {
             const v8i a = cat(lds_read16(dt + od[ks][0]), lds_read16(dt + od[ks][1]));
-            const v8i bv = cat(lds_read16(lds + C::V_OFF + ov[ks][0]), lds_read16(lds + C::V_OFF + ov[ks][1]));
-            dp = mfma<E5M2, E4M3>(a, bv, dp, e8m0(dsr[2 * ks + h]), e8m0(vsr[2 * ks + h]));
+            dp = mfma<E5M2, E4M3>(a, vb[ks], dp, e8m0(dsr[2 * ks + h]), vsc[ks]);
           }
         }
         // lane (key R, h), register v <-> step query 32j + 16h + v
