@@ -420,7 +420,7 @@ static void launch_dkdv_t(const AttnDims& d, Operand qc, Operand qs, Operand kc,
 hipError_t launch_dkdv(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand vc, Operand doc, Operand dos,
                        const float* lse, const float* delta, float* dk, float* dv, hipStream_t s) {
   if (d.dqk == 64 && d.dv == 64) launch_dkdv_t<64, 64>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);
-  else if (d.dqk == 128 && d.dv == 128) launch_dkdv_t<128, 128>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);
+  else if (d.dqk == 128 && d.dv == 128) return launch_dkdv_d128(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);
   else if (d.dqk == 192 && d.dv == 128) launch_dkdv_t<192, 128>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);
   else if (d.dqk == 64 && d.dv == 128) launch_dkdv_t<64, 128>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);
   else if (d.dqk == 128 && d.dv == 64) launch_dkdv_t<128, 64>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);

@@ -1,0 +1,285 @@
+// dK and dV of block-scaled FP8 attention for d_qk = d_v = 128 (key-stationary),
+// on the 16x16x128 scaled matrix instruction.
+//
+// Workgroup = 8 waves over 128 keys; wave w owns keys k0+16w .. k0+16w+15 and
+// forms every product for them, so S, P, dP and dS exist once per (query, key)
+// pair.  A 1-D grid over (key tile, Hkv, B) with key tiles slowest starts the
+// long causal tiles first.  The workgroup walks the query heads of its KV group
+// and, for each, the 128-query steps that can see its keys.  Per step and wave:
+//   8 tiles of 16 queries:  S = Q^<c> K^<c>T,  dP^ = dO^<c> V^<c>T  (one instruction each),
+//                           P = exp(S - LSE),  dS = P (dP^ - delta);
+//   P^<q> (E4M3) and dS^<q> (E5M2) in 32-query blocks;
+//   dV^T += dO^<s>T P^<q>,  dK^T += Q^<s>T dS^<q>  (8 channel tiles each, contraction
+//   over the step's 128 queries).
+// Row m of S tile t is step query qrow(t, m); with that order the 32 results of a
+// lane over the 8 tiles are exactly its 32 K-slots of the dV/dK operand, in slot
+// order, and every 32-query scale block is split over one lane pair (l, l^16).
+// So the codes never leave their lane: per block, one pair max and one exchange
+// that hands the block's scale to the lane that supplies it.
+//
+// The query-side tiles of step i+1 (Q^<c>, dO^<c> rows, Q^<s>, dO^<s> channel
+// rows and all four scale arrays) arrive in the other half of a double LDS
+// buffer by direct global->LDS loads issued at the start of step i; LSE and delta
+// come through registers.  One barrier per step.  dK and dV accumulate in
+// registers over every query head of the group and are written once.
+#include <type_traits>
+
+#include "dm_common.h"
+#include "dm_internal.h"
+
+namespace dm {
+namespace {
+
+constexpr int kD = 128;                  // d_qk = d_v
+constexpr int kNW = 8, kNT = 64 * kNW;
+constexpr int kKT = 16 * kNW;            // keys per workgroup
+constexpr int kQT = 128;                 // queries per step
+// one step's stage (bytes).  Q^<c>/dO^<c> rows and their scales are stored in
+// tile order: LDS row 16t+m holds step query qrow(t, m).
+constexpr int kQC = 0;                   // Q^<c> [128 rows][128], chunks swizzled by tile_slot<128>
+constexpr int kDOC = kQC + kQT * kD;     // dO^<c> rows
+constexpr int kQS = kDOC + kQT * kD;     // Q^<s> [128 channels][128 queries], swizzled
+constexpr int kDOS = kQS + kD * kQT;     // dO^<s>
+constexpr int kQCS = kDOS + kD * kQT;    // Q^<c> scales [128 rows][4 blocks] fp32
+constexpr int kDOCS = kQCS + kQT * 16;   // dO^<c> scales
+constexpr int kQSS = kDOCS + kQT * 16;   // Q^<s> scales [128 channels][4 query blocks]
+constexpr int kDOSS = kQSS + kD * 16;    // dO^<s> scales
+constexpr int kLSE = kDOSS + kD * 16;    // LSE * log2(e) [128], then delta [128]
+constexpr int kSTAGE = kLSE + 2 * kQT * 4;
+static_assert(2 * kSTAGE <= 160 * 1024, "LDS budget");
+
+// step query of row m of S tile t (see the header comment)
+__device__ __forceinline__ int qrow(int t, int m) { return 64 * (t >> 2) + 16 * (m >> 2) + 4 * (t & 3) + (m & 3); }
+
+}  // namespace
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
+    const uint8_t* __restrict__ qc, const float* __restrict__ qcs, const uint8_t* __restrict__ qs,
+    const float* __restrict__ qss, const uint8_t* __restrict__ kc, const float* __restrict__ kcs,
+    const uint8_t* __restrict__ vc, const float* __restrict__ vcs, const uint8_t* __restrict__ doc,
+    const float* __restrict__ docs, const uint8_t* __restrict__ dos, const float* __restrict__ doss,
+    const float* __restrict__ lse, const float* __restrict__ delta, float* __restrict__ dk, float* __restrict__ dv,
+    int Hq, int Hkv, int L, int Lp, float sigma) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kSTAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;              // key column / lane group of the 16x16 tiles
+  const int nkt = Lp / kKT;
+  const int nhb = Hkv * (int)(gridDim.x / (nkt * Hkv));    // Hkv * B
+  const int hk = (int)blockIdx.x % nhb % Hkv, b = (int)blockIdx.x % nhb / Hkv;
+  const int k0 = ((int)blockIdx.x / nhb) * kKT;           // key tiles slowest: long causal tiles first
+  const int G = Hq / Hkv;
+  const int kw0 = k0 + 16 * w;                       // this wave's first key
+  const int key = kw0 + n;                           // this lane's key
+  const int LB = Lp / kBlock;
+  const int64_t khead = (int64_t)b * Hkv + hk;
+  const int64_t qhead0 = (int64_t)b * Hq + (int64_t)hk * G;
+
+  // this wave's K^<c>, V^<c> rows as B operands (key n, channel chunks g and 4+g)
+  v8i kb, vb;
+  int ksc, vsc;
+  {
+    const int64_t kr = khead * Lp + key;
+    kb = cat(*reinterpret_cast<const v4i*>(kc + kr * kD + 16 * g), *reinterpret_cast<const v4i*>(kc + kr * kD + 64 + 16 * g));
+    vb = cat(*reinterpret_cast<const v4i*>(vc + kr * kD + 16 * g), *reinterpret_cast<const v4i*>(vc + kr * kD + 64 + 16 * g));
+    ksc = e8m0(kcs[kr * (kD / kBlock) + g]);
+    vsc = e8m0(vcs[kr * (kD / kBlock) + g]);
+  }
+
+  // ---- direct loads: per wave two 1 KB pieces of each 16 KB tile and one piece of the scales
+  int orow[2], ochan[2];                             // per-lane source offsets (loop invariant)
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 8 * (w + 8 * i) + (lane >> 3);     // LDS row this lane fills
+    const int chunk = tile_slot<kD>(r, lane & 7);    // global 16-byte chunk of that slot
+    orow[i] = qrow(r >> 4, r & 15) * kD + 16 * chunk;
+    ochan[i] = r * Lp + 16 * chunk;
+  }
+  const int sel = w >> 1;                            // 0 Q^<c>, 1 dO^<c>, 2 Q^<s>, 3 dO^<s> scales
+  const int srow = 64 * (w & 1) + lane;
+  const int oscale = sel < 2 ? qrow(srow >> 4, srow & 15) * 16 : srow * LB * 4;
+  const uint8_t* const sbase = reinterpret_cast<const uint8_t*>(sel == 0 ? qcs : sel == 1 ? docs : sel == 2 ? qss : doss);
+  const int sdst = kQCS + 1024 * w;
+  auto issue = [&](int64_t qhead, int q0, uint8_t* st) {
+    const int64_t rowb = (qhead * Lp + q0) * kD;
+    const int64_t chb = qhead * kD * (int64_t)Lp + q0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int dst = 1024 * (w + 8 * i);
+      dma16(qc + rowb + orow[i], st + kQC + dst);
+      dma16(doc + rowb + orow[i], st + kDOC + dst);
+      dma16(qs + chb + ochan[i], st + kQS + dst);
+      dma16(dos + chb + ochan[i], st + kDOS + dst);
+    }
+    const int64_t sb = sel < 2 ? (qhead * Lp + q0) * 16 : qhead * kD * (int64_t)LB * 4 + q0 / 8;
+    dma16(sbase + sb + oscale, st + sdst);
+  };
+  // LSE (in log2 units) and delta of the step's queries through registers
+  float smallv = 0.f;
+  auto load_small = [&](int64_t qhead, int q0) {
+    if (tid < kQT) {
+      const int q = q0 + tid;
+      smallv = q < L ? lse[qhead * L + q] * kLog2e : INFINITY;    // padded queries: P = 0
+    } else if (tid < 2 * kQT) {
+      const int q = q0 + tid - kQT;
+      smallv = q < L ? delta[qhead * L + q] : 0.f;
+    }
+  };
+  auto store_small = [&](uint8_t* st) {
+    if (tid < 2 * kQT) reinterpret_cast<float*>(st + kLSE)[tid] = smallv;
+  };
+
+  v4f accv[kD / 16], acck[kD / 16];                  // dV^T, dK^T channel tiles: reg i <-> channel 16ct+4g+i
+#pragma unroll
+  for (int i = 0; i < kD / 16; ++i) accv[i] = acck[i] = v4f{};
+
+  const float c2 = sigma * kLog2e;
+  const int qstart = CAUSAL ? k0 : 0;
+  const int nsteps = (Lp - qstart) / kQT;
+  const int total = G * nsteps;
+  uint8_t* const stage0 = lds;
+  issue(qhead0, qstart, stage0);
+  load_small(qhead0, qstart);
+  store_small(stage0);
+
+  // LDS read offsets of this lane's operand row (row n of a 16-row tile, chunks g and 4+g)
+  const int ra0 = n * 128 + 16 * tile_slot<kD>(n, g);
+  const int ra1 = n * 128 + 16 * tile_slot<kD>(n, 4 + g);
+
+  auto step = [&](int it, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int hh = it / nsteps;
+    const int q0 = qstart + (it - hh * nsteps) * kQT;
+    uint8_t* const st = stage0 + (it & 1) * kSTAGE;
+    uint8_t* const stn = stage0 + ((it + 1) & 1) * kSTAGE;
+    wait_vmem();
+    __syncthreads();                               // step it staged; the other buffer is free
+    const bool more = it + 1 < total;
+    if (more) {
+      const int hn = (it + 1) / nsteps;
+      const int qn = qstart + (it + 1 - hn * nsteps) * kQT;
+      issue(qhead0 + hn, qn, stn);
+      load_small(qhead0 + hn, qn);
+    }
+
+    if (kw0 < L) {
+      uint32_t pc[8], dc[8];                       // P^<q>, dS^<q> codes: dword t <-> S tile t
+      int kp[2], kd[2];                            // scale exponents of the lane's lo / hi blocks
+      const float* lsep = reinterpret_cast<const float*>(st + kLSE) + 16 * g;
+      const float* delp = lsep + kQT;
+      const float* qcsp = reinterpret_cast<const float*>(st + kQCS) + 4 * n + g;
+      const float* docsp = reinterpret_cast<const float*>(st + kDOCS) + 4 * n + g;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        // tiles 4hf .. 4hf+3: lane (n, g) holds queries 64hf + 16g + 4tt + i
+        float pv[16], sv[16];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const int t = 4 * hf + tt;
+          const v8i aq = cat(lds_read16(st + kQC + 2048 * t + ra0), lds_read16(st + kQC + 2048 * t + ra1));
+          const v4f s = mfma16<E4M3, E4M3>(aq, kb, v4f{}, e8m0(qcsp[64 * t]), ksc);
+          const v8i ad = cat(lds_read16(st + kDOC + 2048 * t + ra0), lds_read16(st + kDOC + 2048 * t + ra1));
+          const v4f dp = mfma16<E5M2, E4M3>(ad, vb, v4f{}, e8m0(docsp[64 * t]), vsc);
+          const v4f l4 = *reinterpret_cast<const v4f*>(lsep + 64 * hf + 4 * tt);
+          const v4f d4 = *reinterpret_cast<const v4f*>(delp + 64 * hf + 4 * tt);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float x = s[i];
+            if constexpr (MASK) {
+              const int q = q0 + 64 * hf + 16 * g + 4 * tt + i;
+              if (key >= L || (CAUSAL && key > q)) x = -INFINITY;
+            }
+            const float p = __builtin_amdgcn_exp2f(fmaf(x, c2, -l4[i]));
+            pv[4 * tt + i] = p;
+            sv[4 * tt + i] = p * (dp[i] - d4[i]);
+          }
+        }
+        // block maxima: the lane's 16 values and its partner's (l ^ 16) form one 32-query block
+        float mp = fmaxf(fmaxf(pv[0], pv[1]), pv[2]);
+        float md = fmaxf(fmaxf(fabsf(sv[0]), fabsf(sv[1])), fabsf(sv[2]));
+#pragma unroll
+        for (int v = 3; v < 15; v += 2) {
+          mp = fmaxf(fmaxf(mp, pv[v]), pv[v + 1]);
+          md = fmaxf(fmaxf(md, fabsf(sv[v])), fabsf(sv[v + 1]));
+        }
+        mp = pair16_max(fmaxf(mp, pv[15]));
+        md = pair16_max(fmaxf(md, fabsf(sv[15])));
+        kp[hf] = scale_exp<E4M3>(mp);
+        kd[hf] = scale_exp<E5M2>(md);
+        const float sp = exp2i(kp[hf]), sd = exp2i(kd[hf]);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          pc[4 * hf + tt] = pack4s<E4M3>(pv[4 * tt], pv[4 * tt + 1], pv[4 * tt + 2], pv[4 * tt + 3], sp);
+          dc[4 * hf + tt] = pack4s<E5M2>(sv[4 * tt], sv[4 * tt + 1], sv[4 * tt + 2], sv[4 * tt + 3], sd);
+        }
+      }
+      // Lane group g supplies the scale of K-block g (queries 32g..32g+31).  Its own
+      // blocks are g/2 (lo) and 2+g/2 (hi): groups 0 and 3 hold theirs; group 1 takes
+      // block 1 from group 3 and group 2 takes block 2 from group 0 (lanes l ^ 32).
+      auto supply = [&](const int* k) {
+        const uint32_t x = (uint32_t)(g == 0 ? k[1] : k[0]);
+        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        const int other = (int)(g == 1 ? r[1] : r[0]);
+        return (g == 0 ? k[0] : g == 3 ? k[1] : other) + 127;
+      };
+      const int sup_p = supply(kp), sup_d = supply(kd);
+      v8i bp, bd;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        bp[i] = (int)pc[i];
+        bd[i] = (int)dc[i];
+      }
+      // dV^T += dO^<s>T P^<q>,  dK^T += Q^<s>T dS^<q>: A = channel rows 16ct+n, query chunks g, 4+g
+      const float* dossp = reinterpret_cast<const float*>(st + kDOSS) + 4 * n + g;
+      const float* qssp = reinterpret_cast<const float*>(st + kQSS) + 4 * n + g;
+#pragma unroll
+      for (int ct = 0; ct < kD / 16; ++ct) {
+        const v8i a = cat(lds_read16(st + kDOS + 2048 * ct + ra0), lds_read16(st + kDOS + 2048 * ct + ra1));
+        accv[ct] = mfma16<E5M2, E4M3>(a, bp, accv[ct], e8m0(dossp[64 * ct]), sup_p);
+      }
+#pragma unroll
+      for (int ct = 0; ct < kD / 16; ++ct) {
+        const v8i a = cat(lds_read16(st + kQS + 2048 * ct + ra0), lds_read16(st + kQS + 2048 * ct + ra1));
+        acck[ct] = mfma16<E4M3, E5M2>(a, bd, acck[ct], e8m0(qssp[64 * ct]), sup_d);
+      }
+    }
+    if (more) store_small(stn);
+  };
+  // per head: the diagonal step for causal (all steps when the tile holds padded
+  // keys) with the mask, then the rest in a loop without mask code
+  const int nmask = (k0 + kKT > L) ? nsteps : (CAUSAL ? 1 : 0);
+  for (int hh = 0, it = 0; hh < G; ++hh) {
+    for (int i = 0; i < nmask; ++i, ++it) step(it, std::true_type{});
+    for (int i = nmask; i < nsteps; ++i, ++it) step(it, std::false_type{});
+  }
+
+  // ---- dK, dV written once per key: lane (n, g), register i of tile ct <-> channel 16ct + 4g + i
+  if (key < L) {
+    float* dkr = dk + (khead * L + key) * kD + 4 * g;
+    float* dvr = dv + (khead * L + key) * kD + 4 * g;
+#pragma unroll
+    for (int ct = 0; ct < kD / 16; ++ct) {
+      *reinterpret_cast<v4f*>(dvr + 16 * ct) = accv[ct];
+      *reinterpret_cast<v4f*>(dkr + 16 * ct) = sigma * acck[ct];
+    }
+  }
+}
+
+hipError_t launch_dkdv_d128(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand vc, Operand doc,
+                            Operand dos, const float* lse, const float* delta, float* dk, float* dv, hipStream_t s) {
+  if (d.dqk != kD || d.dv != kD || d.Lp % kKT != 0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(d.Lp / kKT) * d.Hkv * d.B);
+  if (d.causal)
+    hipLaunchKernelGGL(dkdv_d128_kernel<true>, grid, dim3(kNT), 0, s, qc.codes, qc.scales, qs.codes, qs.scales,
+                       kc.codes, kc.scales, vc.codes, vc.scales, doc.codes, doc.scales, dos.codes, dos.scales, lse,
+                       delta, dk, dv, d.Hq, d.Hkv, d.L, d.Lp, d.sigma);
+  else
+    hipLaunchKernelGGL(dkdv_d128_kernel<false>, grid, dim3(kNT), 0, s, qc.codes, qc.scales, qs.codes, qs.scales,
+                       kc.codes, kc.scales, vc.codes, vc.scales, doc.codes, doc.scales, dos.codes, dos.scales, lse,
+                       delta, dk, dv, d.Hq, d.Hkv, d.L, d.Lp, d.sigma);
+  return hipGetLastError();
+}
+
+}  // namespace dm

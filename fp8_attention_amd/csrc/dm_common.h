@@ -109,6 +109,21 @@ __device__ __forceinline__ v16f mfma(const v8i& a, const v8i& b, const v16f& c, 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, sa, 0, sb);
 }
 
+// 16x16x128 form: lane (n, g = l/16) holds row/column n; its bytes 0-15 are
+// K-slots 16g..16g+15 and bytes 16-31 K-slots 64+16g..64+16g+15, and it supplies
+// the scale of K-block g (slots 32g..32g+31).  Result register i of lane (n, g)
+// is row 4g+i, column n.
+template <int FA, int FB>
+__device__ __forceinline__ v4f mfma16(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, sa, 0, sb);
+}
+
+// Maximum over the lane pair (l, l^16).
+__device__ __forceinline__ float pair16_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Maximum of the 16 accumulator values of one lane (max3 chain).
 __device__ __forceinline__ float max16(const v16f& x) {
   float m = fmaxf(fmaxf(x[0], x[1]), x[2]);

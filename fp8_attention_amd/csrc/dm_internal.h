@@ -34,6 +34,10 @@ hipError_t launch_bwd(const AttnDims& d, Operand q_c, Operand q_s, Operand k_c, 
 hipError_t launch_dkdv(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand vc, Operand doc, Operand dos,
                        const float* lse, const float* delta, float* dk, float* dv, hipStream_t s);
 
+// d_qk = d_v = 128 form of launch_dkdv (attn_dkdv128.hip)
+hipError_t launch_dkdv_d128(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand vc, Operand doc,
+                            Operand dos, const float* lse, const float* delta, float* dk, float* dv, hipStream_t s);
+
 hipError_t launch_dq(const AttnDims& d, Operand qc, Operand kc, Operand ks, Operand vc, Operand doc,
                      const float* lse, const float* delta, float* dq, double* ps, double* pa, hipStream_t s);
 
