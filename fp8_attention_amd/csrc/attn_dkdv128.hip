@@ -19,8 +19,8 @@
 //
 // The query-side tiles of step i+1 (Q^<c>, dO^<c> rows, Q^<s>, dO^<s> channel
 // rows and all four scale arrays) arrive in the other half of a double LDS
-// buffer by direct global->LDS loads issued at the start of step i; LSE and delta
-// come through registers.  One barrier per step.  dK and dV accumulate in
+// buffer by direct global->LDS loads issued during step i, one per S tile (issued
+// all at once, they stall the waves behind them); LSE and delta come through registers.  One barrier per step.  dK and dV accumulate in
 // registers over every query head of the group and are written once.
 #include <type_traits>
 
@@ -102,6 +102,23 @@ __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
   const int oscale = sel < 2 ? qrow(srow >> 4, srow & 15) * 16 : srow * LB * 4;
   const uint8_t* const sbase = reinterpret_cast<const uint8_t*>(sel == 0 ? qcs : sel == 1 ? docs : sel == 2 ? qss : doss);
   const int sdst = kQCS + 1024 * w;
+  // one of the step's nine direct loads of this wave
+  auto issue_part = [&](int part, int64_t qhead, int q0, uint8_t* st) {
+    if (part == 8) {
+      const int64_t sb = sel < 2 ? (qhead * Lp + q0) * 16 : qhead * kD * (int64_t)LB * 4 + q0 / 8;
+      dma16(sbase + sb + oscale, st + sdst);
+      return;
+    }
+    const int i = part >> 2, which = part & 3;
+    const int dst = 1024 * (w + 8 * i);
+    if (which < 2) {
+      const int64_t rowb = (qhead * Lp + q0) * kD;
+      dma16((which == 0 ? qc : doc) + rowb + orow[i], st + (which == 0 ? kQC : kDOC) + dst);
+    } else {
+      const int64_t chb = qhead * kD * (int64_t)Lp + q0;
+      dma16((which == 2 ? qs : dos) + chb + ochan[i], st + (which == 2 ? kQS : kDOS) + dst);
+    }
+  };
   auto issue = [&](int64_t qhead, int q0, uint8_t* st) {
     const int64_t rowb = (qhead * Lp + q0) * kD;
     const int64_t chb = qhead * kD * (int64_t)Lp + q0;
@@ -157,12 +174,10 @@ __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
     wait_vmem();
     __syncthreads();                               // step it staged; the other buffer is free
     const bool more = it + 1 < total;
-    if (more) {
-      const int hn = (it + 1) / nsteps;
-      const int qn = qstart + (it + 1 - hn * nsteps) * kQT;
-      issue(qhead0 + hn, qn, stn);
-      load_small(qhead0 + hn, qn);
-    }
+    const int hn = (it + 1) / nsteps;
+    const int qn = qstart + (it + 1 - hn * nsteps) * kQT;
+    if (more) load_small(qhead0 + hn, qn);
+    if (more && kw0 >= L) issue(qhead0 + hn, qn, stn);
 
     if (kw0 < L) {
       uint32_t pc[8], dc[8];                       // P^<q>, dS^<q> codes: dword t <-> S tile t
@@ -178,6 +193,8 @@ __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
           const int t = 4 * hf + tt;
+          if (more) issue_part(t + (t == 0 ? 8 : 0), qhead0 + hn, qn, stn);   // next step's loads, spread
+          if (more && t == 0) issue_part(0, qhead0 + hn, qn, stn);
           const v8i aq = cat(lds_read16(st + kQC + 2048 * t + ra0), lds_read16(st + kQC + 2048 * t + ra1));
           const v4f s = mfma16<E4M3, E4M3>(aq, kb, v4f{}, e8m0(qcsp[64 * t]), ksc);
           const v8i ad = cat(lds_read16(st + kDOC + 2048 * t + ra0), lds_read16(st + kDOC + 2048 * t + ra1));
