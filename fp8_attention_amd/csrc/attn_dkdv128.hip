@@ -102,47 +102,46 @@ __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
   const int oscale = sel < 2 ? qrow(srow >> 4, srow & 15) * 16 : srow * LB * 4;
   const uint8_t* const sbase = reinterpret_cast<const uint8_t*>(sel == 0 ? qcs : sel == 1 ? docs : sel == 2 ? qss : doss);
   const int sdst = kQCS + 1024 * w;
-  // one of the step's nine direct loads of this wave
-  auto issue_part = [&](int part, int64_t qhead, int q0, uint8_t* st) {
+  // base pointers of one step's loads (wave-uniform)
+  struct Src {
+    const uint8_t *q, *d, *qs, *ds, *sc;
+  };
+  auto sources = [&](int64_t qhead, int q0) {
+    const int64_t rowb = (qhead * Lp + q0) * kD;
+    const int64_t chb = qhead * kD * (int64_t)Lp + q0;
+    Src r;
+    r.q = qc + rowb;
+    r.d = doc + rowb;
+    r.qs = qs + chb;
+    r.ds = dos + chb;
+    r.sc = sbase + (sel < 2 ? rowb / 8 : qhead * kD * (int64_t)LB * 4 + q0 / 8);
+    return r;
+  };
+  // one of the step's nine direct loads of this wave (part is a constant after unrolling)
+  auto issue_part = [&](int part, const Src& sr, uint8_t* st) {
     if (part == 8) {
-      const int64_t sb = sel < 2 ? (qhead * Lp + q0) * 16 : qhead * kD * (int64_t)LB * 4 + q0 / 8;
-      dma16(sbase + sb + oscale, st + sdst);
+      dma16(sr.sc + oscale, st + sdst);
       return;
     }
     const int i = part >> 2, which = part & 3;
     const int dst = 1024 * (w + 8 * i);
-    if (which < 2) {
-      const int64_t rowb = (qhead * Lp + q0) * kD;
-      dma16((which == 0 ? qc : doc) + rowb + orow[i], st + (which == 0 ? kQC : kDOC) + dst);
-    } else {
-      const int64_t chb = qhead * kD * (int64_t)Lp + q0;
-      dma16((which == 2 ? qs : dos) + chb + ochan[i], st + (which == 2 ? kQS : kDOS) + dst);
-    }
+    if (which == 0) dma16(sr.q + orow[i], st + kQC + dst);
+    else if (which == 1) dma16(sr.d + orow[i], st + kDOC + dst);
+    else if (which == 2) dma16(sr.qs + ochan[i], st + kQS + dst);
+    else dma16(sr.ds + ochan[i], st + kDOS + dst);
   };
-  auto issue = [&](int64_t qhead, int q0, uint8_t* st) {
-    const int64_t rowb = (qhead * Lp + q0) * kD;
-    const int64_t chb = qhead * kD * (int64_t)Lp + q0;
+  auto issue = [&](const Src& sr, uint8_t* st) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int dst = 1024 * (w + 8 * i);
-      dma16(qc + rowb + orow[i], st + kQC + dst);
-      dma16(doc + rowb + orow[i], st + kDOC + dst);
-      dma16(qs + chb + ochan[i], st + kQS + dst);
-      dma16(dos + chb + ochan[i], st + kDOS + dst);
-    }
-    const int64_t sb = sel < 2 ? (qhead * Lp + q0) * 16 : qhead * kD * (int64_t)LB * 4 + q0 / 8;
-    dma16(sbase + sb + oscale, st + sdst);
+    for (int part = 0; part < 9; ++part) issue_part(part, sr, st);
   };
-  // LSE (in log2 units) and delta of the step's queries through registers
+  // LSE (in log2 units) and delta of the step's queries through registers (threads
+  // 0-127 and 128-255; the others load an in-range value they do not store)
   float smallv = 0.f;
   auto load_small = [&](int64_t qhead, int q0) {
-    if (tid < kQT) {
-      const int q = q0 + tid;
-      smallv = q < L ? lse[qhead * L + q] * kLog2e : INFINITY;    // padded queries: P = 0
-    } else if (tid < 2 * kQT) {
-      const int q = q0 + tid - kQT;
-      smallv = q < L ? delta[qhead * L + q] : 0.f;
-    }
+    const int q = q0 + (tid & (kQT - 1));
+    const bool is_lse = tid < kQT;
+    const float x = (is_lse ? lse : delta)[qhead * L + min(q, L - 1)];
+    smallv = q < L ? (is_lse ? x * kLog2e : x) : (is_lse ? INFINITY : 0.f);   // padded queries: P = 0
   };
   auto store_small = [&](uint8_t* st) {
     if (tid < 2 * kQT) reinterpret_cast<float*>(st + kLSE)[tid] = smallv;
@@ -155,9 +154,8 @@ __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
   const float c2 = sigma * kLog2e;
   const int qstart = CAUSAL ? k0 : 0;
   const int nsteps = (Lp - qstart) / kQT;
-  const int total = G * nsteps;
   uint8_t* const stage0 = lds;
-  issue(qhead0, qstart, stage0);
+  issue(sources(qhead0, qstart), stage0);
   load_small(qhead0, qstart);
   store_small(stage0);
 
@@ -165,19 +163,22 @@ __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
   const int ra0 = n * 128 + 16 * tile_slot<kD>(n, g);
   const int ra1 = n * 128 + 16 * tile_slot<kD>(n, 4 + g);
 
-  auto step = [&](int it, auto mask_tag) {
+  // step i of query head hh (running index it); the loads issued during it are those
+  // of the next step, or again this step's after the last one (never read)
+  auto step = [&](int it, int hh, int i, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const int hh = it / nsteps;
-    const int q0 = qstart + (it - hh * nsteps) * kQT;
+    const int q0 = qstart + i * kQT;
     uint8_t* const st = stage0 + (it & 1) * kSTAGE;
     uint8_t* const stn = stage0 + ((it + 1) & 1) * kSTAGE;
     wait_vmem();
     __syncthreads();                               // step it staged; the other buffer is free
-    const bool more = it + 1 < total;
-    const int hn = (it + 1) / nsteps;
-    const int qn = qstart + (it + 1 - hn * nsteps) * kQT;
-    if (more) load_small(qhead0 + hn, qn);
-    if (more && kw0 >= L) issue(qhead0 + hn, qn, stn);
+    const bool head_end = i + 1 == nsteps;
+    const bool more = !(head_end && hh + 1 == G);
+    const int64_t nqh = qhead0 + hh + (head_end && more ? 1 : 0);
+    const int nq0 = !more ? q0 : head_end ? qstart : q0 + kQT;
+    const Src nx = sources(nqh, nq0);
+    load_small(nqh, nq0);
+    if (kw0 >= L) issue(nx, stn);
 
     if (kw0 < L) {
       uint32_t pc[8], dc[8];                       // P^<q>, dS^<q> codes: dword t <-> S tile t
@@ -193,8 +194,8 @@ __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
           const int t = 4 * hf + tt;
-          if (more) issue_part(t + (t == 0 ? 8 : 0), qhead0 + hn, qn, stn);   // next step's loads, spread
-          if (more && t == 0) issue_part(0, qhead0 + hn, qn, stn);
+          issue_part(t + (t == 0 ? 8 : 0), nx, stn);   // next step's loads, spread over the tiles
+          if (t == 0) issue_part(0, nx, stn);
           const v8i aq = cat(lds_read16(st + kQC + 2048 * t + ra0), lds_read16(st + kQC + 2048 * t + ra1));
           const v4f s = mfma16<E4M3, E4M3>(aq, kb, v4f{}, e8m0(qcsp[64 * t]), ksc);
           const v8i ad = cat(lds_read16(st + kDOC + 2048 * t + ra0), lds_read16(st + kDOC + 2048 * t + ra1));
@@ -262,16 +263,17 @@ __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
         acck[ct] = mfma16<E4M3, E5M2>(a, bd, acck[ct], e8m0(qssp[64 * ct]), sup_d);
       }
     }
-    if (more) store_small(stn);
+    store_small(stn);
   };
   // per head: the diagonal step for causal (all steps when the tile holds padded
   // keys) with the mask, then the rest in a loop without mask code
   const int nmask = (k0 + kKT > L) ? nsteps : (CAUSAL ? 1 : 0);
   for (int hh = 0, it = 0; hh < G; ++hh) {
-    for (int i = 0; i < nmask; ++i, ++it) step(it, std::true_type{});
-    for (int i = nmask; i < nsteps; ++i, ++it) step(it, std::false_type{});
+    for (int i = 0; i < nmask; ++i, ++it) step(it, hh, i, std::true_type{});
+    for (int i = nmask; i < nsteps; ++i, ++it) step(it, hh, i, std::false_type{});
   }
 
+  wait_vmem();                                     // the last step's (unused) loads
   // ---- dK, dV written once per key: lane (n, g), register i of tile ct <-> channel 16ct + 4g + i
   if (key < L) {
     float* dkr = dk + (khead * L + key) * kD + 4 * g;

@@ -176,8 +176,15 @@ __device__ __forceinline__ int tile_slot(int row, int c) {
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
+// Issued from inline assembly rather than __builtin_amdgcn_global_load_lds: with the
+// builtin in a kernel the compiler turns every LDS wait into lgkmcnt(0), so reads
+// prefetched for the next tile are waited for together with the current ones.  The
+// hardware tracks these loads with VM_CNT only; every kernel waits for them
+// explicitly (wait_vmem) before the barrier that publishes a buffer.  The nop is
+// the wait state required between the M0 write and the load that uses it.
 __device__ __forceinline__ void dma16(const void* g, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((lds_void*)lds_base));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
 }
 // wait for this wave's outstanding global loads (including direct-to-LDS ones)
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
