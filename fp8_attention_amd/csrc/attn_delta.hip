@@ -3,8 +3,13 @@
 // stale / dO-matched: delta_i = sum_k x_ik O_ik with x = dO (bf16, before its
 //   cast) or x = dO^<c> (decoded E5M2 codes times block scales).  One pass over
 //   O and x with 16-byte loads; bound by HBM bandwidth.
-// matched (Delta-Matching): delta_i = sum_j P_ij dP^_ij with P = exp(S - LSE)
-//   recomputed in FP32 and dP^ = dO^<c> V^<c>^T on FP8 matrix cores.  Same tiling
+// matched (Delta-Matching): delta_i = sum_j P_ij dP^_ij / sum_j P_ij with
+//   P = exp(S - LSE) recomputed in FP32 and dP^ = dO^<c> V^<c>^T on FP8 matrix
+//   cores.  The denominator is 1 in exact arithmetic (P is the softmax); with P
+//   rebuilt from the FP32-rounded LSE it drifts from 1 by up to ~1e-5 on long,
+//   near-saturated rows, and dividing by the sum the dQ kernel reproduces bit for
+//   bit (same products, same exp2) keeps sum_j dS_ij = 0 in the kernels' own
+//   arithmetic, which is the property the correction exists for.  Same tiling
 //   as the forward: 8 waves x 32 queries, 128-key chunks streamed through LDS;
 //   the S^T and dP^T tiles share one layout (query per lane pair, 16 keys per
 //   lane), so the product and its row sum stay in registers until one pair
@@ -207,7 +212,7 @@ __global__ __launch_bounds__(64 * kDelWaves) void delta_matched_kernel(
 
   const float c2 = sigma * kLog2e;
   const float l2 = (live && qi < L) ? lse[qhead * L + qi] * kLog2e : 0.f;
-  double acc = 0.0;                              // FP32 per chunk, FP64 across chunks
+  double acc = 0.0, psum = 0.0;                  // FP32 per chunk, FP64 across chunks
   const int qlast = min(q0 + kDelQ, Lp) - 1;
   const int nchunks = CAUSAL ? (qlast / kChunk + 1) : Lp / kChunk;
   const int wlast = CAUSAL ? min(nchunks - 1, (qw + 31) / kChunk) : nchunks - 1;
@@ -258,20 +263,27 @@ __global__ __launch_bounds__(64 * kDelWaves) void delta_matched_kernel(
           if (kk >= L || (CAUSAL && kk > qi)) s[t][v] = -INFINITY;
         }
     }
-    float cacc = 0.f;
+    float cacc = 0.f, pc = 0.f;
     const int nb = (c + 1) & 1;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) cacc = fmaf(__builtin_amdgcn_exp2f(fmaf(s[t][v], c2, -l2)), dp[t][v], cacc);
+      for (int v = 0; v < 16; ++v) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[t][v], c2, -l2));
+        cacc = fmaf(p, dp[t][v], cacc);
+        pc += p;
+      }
       // tile t of chunk c+1 (unused past this wave's last chunk)
       tiles(nb, t, s[t], dp[t]);
     }
     acc += (double)cacc;
+    psum += (double)pc;
   }
   if (!live) return;
   acc = pair_sum_d(acc);
-  if (qi < L && h == 0) delta[qhead * L + qi] = (float)acc;
+  psum = pair_sum_d(psum);
+  // divided by the row's own sum of P (see the header)
+  if (qi < L && h == 0) delta[qhead * L + qi] = psum > 0.0 ? (float)(acc / psum) : 0.f;
 }
 
 template <int DQK, int DV>

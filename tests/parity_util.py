@@ -85,3 +85,16 @@ def compare(name: str, gpu, ref: np.ndarray, allow=None, rel: float = REL_TOL, m
     if norm_rel is not None:
         assert nrel <= norm_rel, f"{name}: norm-wise relative error {nrel:.3e} > {norm_rel:.1e} ({stats})"
     return stats
+
+
+def oracle_head_chain(q, k, v, do, shp: A.Shape, rows) -> dict:
+    """Oracle chain (quantize, forward, matched delta with its bound, backward, with
+    radii) for one query head given as float64 arrays [1, 1, L, d]; for the
+    full-size tests, which run one head per worker process."""
+    qops = A.quantize_operands(q, k, v, do)
+    ops = A.decode_operands(qops, shp.seqlen)
+    f = A.forward(ops, shp, rows=rows, radius=True)
+    derr = A.delta_bound(ops, shp, "matched", lse=f["lse"], lse_err=f["b_lse"], rows=rows)
+    d = A.delta(ops, shp, "matched", lse=f["lse"], rows=rows)
+    r = A.backward(ops, shp, f["lse"], d, rows=rows, radius=True, delta_err=derr, lse_err=f["b_lse"])
+    return {"qops": qops, "fwd": f, "delta": d, "derr": derr, "bwd": r}

@@ -1,0 +1,139 @@
+"""GPU parity at the full workload sizes, in the call sequence bench.py times.
+
+The GPU runs the whole problem (quantize, forward, matched delta, dK/dV, dQ on
+preallocated outputs, the same calls as bench.py).  The oracle cannot redo a
+full 8K or 64K problem in reasonable time, so it checks a sample it can compute
+exactly: one batch entry and KV group (the last of each, so the highest head and
+batch offsets are exercised), and within it
+  * FP8 codes and scales of every operand of the group: bit-exact;
+  * O, LSE, delta and dQ on sampled 32-row blocks (the first, the last and a
+    spread of others) plus a tail of the sequence;
+  * dK and dV on the keys of that tail: under causal masking only rows at or
+    after a key reach it, so the tail's rows determine those keys completely.
+The same elementwise and norm-wise bars as the small-size tests apply.  The
+matched-mode row sums |sum_j dS_ij| <= 1e-5 sum_j |P_ij dP_ij| are checked on
+every row of the full problem from the kernel's probe (a property that needs no
+oracle).
+"""
+import concurrent.futures as cf
+import multiprocessing
+import os
+import sys
+import time
+
+import numpy as np
+import pytest
+import torch
+
+from fp8_attention_amd import workloads as W
+from oracle import attention as A
+from tests import parity_util as U
+
+pytestmark = pytest.mark.gpu
+
+# workload -> (rows of the tail, number of sampled 32-row blocks before it).  The oracle
+# runs one query head per worker process (spawned: no GPU state crosses over).
+CASES = {
+    "gqa_4k": (256, 4),
+    "gqa_8k": (256, 4),
+    "gqa_64k": (64, 1),
+    "mla_4k": (256, 4),
+}
+
+
+def _log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _rows(L: int, tail: int, nblocks: int):
+    """32-aligned sampled row ranges: nblocks blocks spread from row 0 to just before
+    the tail, and the tail [L - tail, L)."""
+    t0 = L - tail
+    starts = sorted({int(s) // 32 * 32 for s in np.linspace(0, t0 - 32, nblocks)})
+    return [(s, s + 32) for s in starts] + [(t0, L)]
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("name", list(CASES))
+def test_fullsize_chain_sampled(name):
+    from fp8_attention_amd import api
+    w = W.WORKLOADS[name]
+    tail, nblocks = CASES[name]
+    B, Hq, Hkv, L, G = w.batch, w.heads_q, w.heads_kv, w.seqlen, w.group
+    _log(f"[fullsize] {name}: {w}")
+    inputs = W.generate(w)
+    dev = {n: t.cuda() for n, t in inputs.items()}
+    shape = api.AttnShape(B, Hq, Hkv, L, w.d_qk, w.d_v, w.causal)
+    ops = api.quantize_operands(dev["q"], dev["k"], dev["v"], dev["do"])
+    o = torch.empty((B, Hq, L, w.d_v), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq, L), dtype=torch.float32, device="cuda")
+    delta = torch.empty_like(lse)
+    dq = torch.empty((B, Hq, L, w.d_qk), dtype=torch.float32, device="cuda")
+    dk = torch.empty((B, Hkv, L, w.d_qk), dtype=torch.float32, device="cuda")
+    dv = torch.empty((B, Hkv, L, w.d_v), dtype=torch.float32, device="cuda")
+    # the timed step of bench.py
+    api.attn_fwd(shape, ops["q_c"], ops["k_c"], ops["v_s"], o=o, lse=lse)
+    api.attn_delta(shape, "matched", do_c=ops["do_c"], q_c=ops["q_c"], k_c=ops["k_c"], v_c=ops["v_c"],
+                   lse=lse, out=delta)
+    api.attn_bwd_dkdv(shape, ops, lse, delta, dk=dk, dv=dv)
+    api.attn_bwd_dq(shape, ops, lse, delta, dq=dq)
+    # the row-sum probe over the whole problem (the probing dQ instance)
+    pr = api.attn_bwd_dq(shape, ops, lse, delta, probe=True)
+    torch.cuda.synchronize()
+    _log("   gpu done")
+    rs, ra = U.to64(pr["rowsum"]), U.to64(pr["rowabs"])
+    ratio = np.abs(rs) / np.maximum(ra, 1e-300)
+    assert np.all(np.abs(rs) <= U.ROWSUM_TOL * ra), f"row-sum ratio max {float(ratio.max()):.3e}"
+    _log(f"   row sums: max |sum dS| / sum |P dP| = {float(ratio.max()):.2e} over {rs.size} rows")
+
+    # oracle on the last batch entry and KV group, one query head per process
+    b, g = B - 1, Hkv - 1
+    sel = U.select_group(inputs, w, b, g)
+    shp = A.Shape(1, 1, 1, L, w.d_qk, w.d_v, bool(w.causal), shape.sigma)
+    rows = _rows(L, tail, nblocks)
+    t0 = time.perf_counter()
+    k64, v64 = U.to64(sel["k"]), U.to64(sel["v"])
+    qh = [U.to64(sel["q"][:, j:j + 1]) for j in range(G)]
+    dh = [U.to64(sel["do"][:, j:j + 1]) for j in range(G)]
+    ctx = multiprocessing.get_context("spawn")
+    with cf.ProcessPoolExecutor(max_workers=min(G, 16, os.cpu_count() or 1), mp_context=ctx) as ex:
+        futs = [ex.submit(U.oracle_head_chain, qh[j], k64, v64, dh[j], shp, rows) for j in range(G)]
+        heads = [fu.result() for fu in futs]
+    _log(f"   oracle {time.perf_counter() - t0:.1f} s on rows {rows} of {G} head(s)")
+    cat = lambda get: np.concatenate([get(h) for h in heads], axis=1)       # noqa: E731
+    f = {n: cat(lambda h, n=n: h["fwd"][n]) for n in ("o", "lse", "r_o", "b_o", "b_lse")}
+    d, derr = cat(lambda h: h["delta"]), cat(lambda h: h["derr"])
+    r = {n: cat(lambda h, n=n: h["bwd"][n]) for n in ("dq", "r_dq", "b_dq")}
+    for n in ("dk", "dv", "r_dk", "b_dk", "r_dv", "b_dv"):
+        r[n] = sum(h["bwd"][n] for h in heads)                 # GQA: summed over the group's heads
+    hs = slice(g * G, (g + 1) * G)
+    L32 = (L + 31) // 32 * 32
+    for n in heads[0]["qops"]:
+        if n[0] in "qd":                                       # q_*, do_*: per query head
+            codes = np.concatenate([h["qops"][n][0] for h in heads], axis=1)
+            scales = np.concatenate([h["qops"][n][1] for h in heads], axis=1)
+            hsel = hs
+        else:                                                  # k_*, v_*: the KV head
+            codes, scales = heads[0]["qops"][n]
+            hsel = slice(g, g + 1)
+        gc = ops[n].codes[b:b + 1, hsel].cpu().numpy()
+        gs = ops[n].scales[b:b + 1, hsel].cpu().numpy().astype(np.float64)
+        if n.endswith("_c"):
+            gc, gs = gc[..., :L, :], gs[..., :L, :]
+        else:
+            gc, gs = gc[..., :L32], gs[..., :L32 // 32]
+        assert np.array_equal(gc, codes), n + " codes"
+        assert np.array_equal(gs, scales), n + " scales"
+
+    gsl = (slice(b, b + 1), hs)
+    U.compare("O", o[gsl], f["o"], allow=f["r_o"] + f["b_o"], norm_rel=U.NORM_TOL)
+    U.compare("LSE", lse[gsl], f["lse"], allow=f["b_lse"], rel=0.0)
+    U.compare("delta", delta[gsl], d, allow=derr, rel=0.0)
+    _log("   ", U.compare("dq", dq[gsl], r["dq"], allow=r["r_dq"] + r["b_dq"], norm_rel=U.NORM_TOL))
+    keys = np.zeros((1, 1, L, 1), dtype=bool)
+    keys[:, :, L - tail:] = True
+    ksl = (slice(b, b + 1), slice(g, g + 1))
+    for n in ("dk", "dv"):
+        t = dk if n == "dk" else dv
+        _log("   ", U.compare(n, t[ksl], r[n], allow=r["r_" + n] + r["b_" + n], norm_rel=U.NORM_TOL,
+                              mask=np.broadcast_to(keys, r[n].shape)))
