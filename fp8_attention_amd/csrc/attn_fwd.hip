@@ -62,10 +62,9 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_kernel(
   const int lane = tid & 63, w = tid >> 6;
   const int R = lane & 31, h = lane >> 5;
   const int nqt = (Lp + kFwdQ - 1) / kFwdQ;
-  const int nhb = Hq * (int)(gridDim.x / (nqt * Hq));      // Hq * B
-  const int tr = (int)blockIdx.x / nhb, hb = (int)blockIdx.x % nhb;
-  const int qt = CAUSAL ? (nqt - 1 - tr) : tr;            // longest causal tiles dispatched first
-  const int hq = hb % Hq, b = hb / Hq;
+  const QueryItem item = query_item((int)blockIdx.x, nqt, Hq, Hkv, (int)gridDim.x / (nqt * Hq));
+  const int qt = CAUSAL ? (nqt - 1 - item.tr) : item.tr;  // longest causal tiles first
+  const int hq = item.hq, b = item.b;
   const int hk = hq / (Hq / Hkv);
   const int q0 = qt * kFwdQ;
   const int qw = q0 + 32 * w;                 // first query of this wave

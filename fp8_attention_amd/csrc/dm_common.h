@@ -175,6 +175,27 @@ __device__ __forceinline__ int tile_slot(int row, int c) {
   }
 }
 
+// Work item (query-tile rank tr, query head hq, batch b) of workgroup bid in a 1-D
+// grid of nqt * Hq * nb query-stationary workgroups.  Workgroups are dealt to the
+// 8 XCDs in turn (bid % 8), each with its own L2: when the (batch, KV group) units
+// divide evenly, XCD x takes whole units, one after another, so the query heads
+// that share a K/V stream and all their query tiles run behind one L2.  Within a
+// unit tr runs fastest over the heads and slowest over tiles, so with tr mapped to
+// the longest causal tiles first the long work starts early.
+struct QueryItem {
+  int tr, hq, b;
+};
+__device__ __forceinline__ QueryItem query_item(int bid, int nqt, int Hq, int Hkv, int nb) {
+  const int G = Hq / Hkv, NG = nb * Hkv;
+  if (NG % 8 == 0) {
+    const int per = G * nqt;                   // workgroups of one (batch, KV group)
+    const int s = bid / 8, gi = (bid % 8) * (NG / 8) + s / per, r = s % per;
+    return {r / G, (gi % Hkv) * G + r % G, gi / Hkv};
+  }
+  const int nhb = Hq * nb;
+  return {bid / nhb, bid % nhb % Hq, bid % nhb / Hq};
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
 // Issued from inline assembly rather than __builtin_amdgcn_global_load_lds: with the
 // builtin in a kernel the compiler turns every LDS wait into lgkmcnt(0), so reads
