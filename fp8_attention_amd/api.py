@@ -203,24 +203,35 @@ def attn_bwd_dkdv(shape: AttnShape, ops: dict, lse: torch.Tensor, delta: torch.T
 
 
 def attn_bwd_dq(shape: AttnShape, ops: dict, lse: torch.Tensor, delta: torch.Tensor, probe: bool = False,
-                dq: Optional[torch.Tensor] = None) -> dict:
-    """dm_attn_bwd_dq -> {"dq"} float32 (+ "rowsum","rowabs" probes): the query-stationary half."""
+                dq: Optional[torch.Tensor] = None, probe_cast: bool = False) -> dict:
+    """dm_attn_bwd_dq -> {"dq"} float32 (+ "rowsum","rowabs" probes): the query-stationary half.
+
+    With ``probe_cast`` (dm_attn_bwd_dq_probes) also "rowsum_cast": the row sums of dS
+    after its E5M2 cast along keys (implies ``probe``)."""
     dev = lse.device
     B, Hq, L = shape.batch, shape.heads_q, shape.seqlen
     if dq is None:
         dq = torch.empty((B, Hq, L, shape.d_qk), dtype=torch.float32, device=dev)
-    ps = pa = None
+    probe = probe or probe_cast
+    ps = pa = pc = None
     if probe:
         ps = torch.empty((B, Hq, L), dtype=torch.float64, device=dev)
         pa = torch.empty((B, Hq, L), dtype=torch.float64, device=dev)
     cs = shape.c()
-    st = _lib.load().dm_attn_bwd_dq(ctypes.byref(cs), ops["q_c"].c(), ops["k_c"].c(), ops["k_s"].c(),
-                                    ops["v_c"].c(), ops["do_c"].c(), lse.data_ptr(), delta.data_ptr(),
-                                    dq.data_ptr(), _ptr(ps), _ptr(pa), _stream(lse))
-    _lib.check(st, "dm_attn_bwd_dq")
+    args = (ctypes.byref(cs), ops["q_c"].c(), ops["k_c"].c(), ops["k_s"].c(), ops["v_c"].c(), ops["do_c"].c(),
+            lse.data_ptr(), delta.data_ptr(), dq.data_ptr(), _ptr(ps), _ptr(pa))
+    if probe_cast:
+        pc = torch.empty((B, Hq, L), dtype=torch.float64, device=dev)
+        st = _lib.load().dm_attn_bwd_dq_probes(*args, _ptr(pc), _stream(lse))
+        _lib.check(st, "dm_attn_bwd_dq_probes")
+    else:
+        st = _lib.load().dm_attn_bwd_dq(*args, _stream(lse))
+        _lib.check(st, "dm_attn_bwd_dq")
     out = {"dq": dq}
     if probe:
         out["rowsum"], out["rowabs"] = ps, pa
+    if probe_cast:
+        out["rowsum_cast"] = pc
     return out
 
 

@@ -25,9 +25,9 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 EXTRA = {src: ["-fno-honor-nans"]
          for src in ("attn_fwd.hip", "attn_delta.hip", "attn_bwd.hip", "attn_dq.hip", "attn_dq_wide.hip",
                      "attn_dkdv128.hip")}
-# dK/dV and dQ run one wave per SIMD with their accumulators in AGPRs; keep the score
-# tiles' MFMA results in VGPRs so the FP32 softmax work does not shuttle them through
-# AGPRs.  (The d_qk=192/d_v=128 dQ instance is built without it: the compiler fails on it.)
+# The generic dK/dV kernel and the dQ kernels: keep MFMA results in VGPRs so the FP32
+# softmax work on the score tiles does not shuttle them through AGPRs.  (The
+# d_qk=192/d_v=128 dQ instance is built without it: the compiler fails on it.)
 EXTRA["attn_bwd.hip"] += ["-mllvm", "--amdgpu-mfma-vgpr-form"]
 EXTRA["attn_dq.hip"] += ["-mllvm", "--amdgpu-mfma-vgpr-form"]
 

@@ -169,7 +169,23 @@ dm_status dm_attn_bwd_dq(const dm_attn_shape* shape, dm_fp8_operand q_c, dm_fp8_
   if (probe_rowsum_ds && (st = check_ptrs({probe_rowsum_ds, probe_rowsum_abs_pdp})) != DM_OK) return st;
   if (shape->seqlen == 0) return DM_OK;
   return hip_status(dm::launch_dq(dims_of(shape), op(q_c), op(k_c), op(k_s), op(v_c), op(do_c), lse, delta, dq,
-                                  probe_rowsum_ds, probe_rowsum_abs_pdp, stream));
+                                  probe_rowsum_ds, probe_rowsum_abs_pdp, nullptr, stream));
+}
+
+dm_status dm_attn_bwd_dq_probes(const dm_attn_shape* shape, dm_fp8_operand q_c, dm_fp8_operand k_c,
+                                dm_fp8_operand k_s, dm_fp8_operand v_c, dm_fp8_operand do_c, const float* lse,
+                                const float* delta, float* dq, double* probe_rowsum_ds, double* probe_rowsum_abs_pdp,
+                                double* probe_rowsum_ds_cast, hipStream_t stream) {
+  dm_status st = check_shape(shape);
+  if (st != DM_OK) return st;
+  const dm_fp8_operand ops[5] = {q_c, k_c, k_s, v_c, do_c};
+  for (const auto& x : ops)
+    if ((st = check_operand(x)) != DM_OK) return st;
+  if ((st = check_ptrs({lse, delta, dq, probe_rowsum_ds, probe_rowsum_abs_pdp, probe_rowsum_ds_cast})) != DM_OK)
+    return st;
+  if (shape->seqlen == 0) return DM_OK;
+  return hip_status(dm::launch_dq(dims_of(shape), op(q_c), op(k_c), op(k_s), op(v_c), op(do_c), lse, delta, dq,
+                                  probe_rowsum_ds, probe_rowsum_abs_pdp, probe_rowsum_ds_cast, stream));
 }
 
 }  // extern "C"

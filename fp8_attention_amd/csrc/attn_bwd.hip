@@ -434,7 +434,7 @@ hipError_t launch_bwd(const AttnDims& d, Operand qc, Operand qs, Operand kc, Ope
                       double* ps, double* pa, hipStream_t s) {
   hipError_t e = launch_dkdv(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);
   if (e != hipSuccess) return e;
-  return launch_dq(d, qc, kc, ks, vc, doc, lse, delta, dq, ps, pa, s);
+  return launch_dq(d, qc, kc, ks, vc, doc, lse, delta, dq, ps, pa, nullptr, s);
 }
 
 __global__ void fill_zero_kernel(uint64_t* p, int64_t n) {

@@ -47,7 +47,8 @@ __global__ __launch_bounds__(64 * dq_waves<PROBE>()) void dq_kernel(
     const float* __restrict__ kcs, const uint8_t* __restrict__ vc, const float* __restrict__ vcs,
     const uint8_t* __restrict__ kst, const float* __restrict__ ksts, const uint8_t* __restrict__ doc,
     const float* __restrict__ docs, const float* __restrict__ lse, const float* __restrict__ delta,
-    float* __restrict__ dq, double* __restrict__ psum, double* __restrict__ pabs, int Hq, int Hkv, int L, int Lp,
+    float* __restrict__ dq, double* __restrict__ psum, double* __restrict__ pabs, double* __restrict__ pcast, int Hq,
+    int Hkv, int L, int Lp,
     float sigma) {
   constexpr int kDqWaves = dq_waves<PROBE>(), kDqQ = 32 * kDqWaves;
   using C = DqLds<DQK, DV, kDqWaves>;
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(64 * dq_waves<PROBE>()) void dq_kernel(
   const float c2 = sigma * kLog2e;
   const float l2 = (live && qi < L) ? lse[qhead * L + qi] * kLog2e : INFINITY;   // pad rows: P = 0
   const float del = (live && qi < L) ? delta[qhead * L + qi] : 0.f;
-  double rsum = 0.0, rabs = 0.0;                // probes: FP32 per chunk, FP64 across chunks
+  double rsum = 0.0, rabs = 0.0, rcast = 0.0;   // probes: FP32 per chunk, FP64 across chunks
   v16f acc[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) acc[ct] = v16f{};
@@ -204,7 +205,7 @@ __global__ __launch_bounds__(64 * dq_waves<PROBE>()) void dq_kernel(
     const float* tsp = reinterpret_cast<const float*>(vp + C::OFF_TS);
     v8i dsb[2];
     int dssc[2] = {0, 0};
-    float csum = 0.f, cabs = 0.f;
+    float csum = 0.f, cabs = 0.f, ccast = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       // dP^T tile t of chunk c
@@ -242,6 +243,17 @@ __global__ __launch_bounds__(64 * dq_waves<PROBE>()) void dq_kernel(
       for (int g = 0; g < 4; ++g)
         dsb[t >> 1][4 * (t & 1) + g] = (int)pack4s<E5M2>(d[4 * g], d[4 * g + 1], d[4 * g + 2], d[4 * g + 3], sc);
       if ((t & 1) == h) dssc[t >> 1] = k + 127;
+      if constexpr (PROBE) {
+        // the row's sum after the cast: the decoded E5M2 codes of this tile times its scale
+        float cs = 0.f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int code = dsb[t >> 1][4 * (t & 1) + g];
+          cs += __builtin_amdgcn_cvt_f32_bf8(code, 0) + __builtin_amdgcn_cvt_f32_bf8(code, 1) +
+                __builtin_amdgcn_cvt_f32_bf8(code, 2) + __builtin_amdgcn_cvt_f32_bf8(code, 3);
+        }
+        ccast += cs * sc;
+      }
       if (t == 1 || t == 3) {
         // dS^<k> of key half st complete: dQ^T += K^<s>^T dS^<k>^T over those 64 keys
         const int st = t >> 1;
@@ -258,6 +270,7 @@ __global__ __launch_bounds__(64 * dq_waves<PROBE>()) void dq_kernel(
     if constexpr (PROBE) {
       rsum += (double)csum;
       rabs += (double)cabs;
+      rcast += (double)ccast;
     }
   };
   auto sync_and_issue = [&](int c) {
@@ -289,6 +302,7 @@ __global__ __launch_bounds__(64 * dq_waves<PROBE>()) void dq_kernel(
   if constexpr (PROBE) {
     rsum = pair_sum_d(rsum);
     rabs = pair_sum_d(rabs);
+    rcast = pair_sum_d(rcast);
   }
   if (qi < L) {
     float* row = dq + (qhead * L + qi) * DQK + 4 * h;
@@ -304,6 +318,7 @@ __global__ __launch_bounds__(64 * dq_waves<PROBE>()) void dq_kernel(
       if (h == 0) {
         psum[qhead * L + qi] = rsum;
         pabs[qhead * L + qi] = rabs;
+        if (pcast) pcast[qhead * L + qi] = rcast;
       }
     }
   }
@@ -311,29 +326,32 @@ __global__ __launch_bounds__(64 * dq_waves<PROBE>()) void dq_kernel(
 
 template <int DQK, int DV, bool CAUSAL, bool PROBE>
 static void launch_dq_t4(const AttnDims& d, Operand qc, Operand kc, Operand ks, Operand vc, Operand doc,
-                         const float* lse, const float* delta, float* dq, double* ps, double* pa, hipStream_t s) {
+                         const float* lse, const float* delta, float* dq, double* ps, double* pa, double* pc,
+                         hipStream_t s) {
   constexpr int kDqQ = 32 * dq_waves<PROBE>();
   dim3 grid((unsigned)((d.Lp + kDqQ - 1) / kDqQ) * d.Hq * d.B);
   hipLaunchKernelGGL((dq_kernel<DQK, DV, CAUSAL, PROBE>), grid, dim3(2 * kDqQ), 0, s, qc.codes, qc.scales, kc.codes,
                      kc.scales, vc.codes, vc.scales, ks.codes, ks.scales, doc.codes, doc.scales, lse, delta, dq, ps,
-                     pa, d.Hq, d.Hkv, d.L, d.Lp, d.sigma);
+                     pa, pc, d.Hq, d.Hkv, d.L, d.Lp, d.sigma);
 }
 
 template <int DQK, int DV>
 static void launch_dq_t(const AttnDims& d, Operand qc, Operand kc, Operand ks, Operand vc, Operand doc,
-                        const float* lse, const float* delta, float* dq, double* ps, double* pa, hipStream_t s) {
+                        const float* lse, const float* delta, float* dq, double* ps, double* pa, double* pc,
+                         hipStream_t s) {
   if (d.causal) {
-    if (ps) launch_dq_t4<DQK, DV, true, true>(d, qc, kc, ks, vc, doc, lse, delta, dq, ps, pa, s);
-    else launch_dq_t4<DQK, DV, true, false>(d, qc, kc, ks, vc, doc, lse, delta, dq, ps, pa, s);
+    if (ps) launch_dq_t4<DQK, DV, true, true>(d, qc, kc, ks, vc, doc, lse, delta, dq, ps, pa, pc, s);
+    else launch_dq_t4<DQK, DV, true, false>(d, qc, kc, ks, vc, doc, lse, delta, dq, ps, pa, pc, s);
   } else {
-    if (ps) launch_dq_t4<DQK, DV, false, true>(d, qc, kc, ks, vc, doc, lse, delta, dq, ps, pa, s);
-    else launch_dq_t4<DQK, DV, false, false>(d, qc, kc, ks, vc, doc, lse, delta, dq, ps, pa, s);
+    if (ps) launch_dq_t4<DQK, DV, false, true>(d, qc, kc, ks, vc, doc, lse, delta, dq, ps, pa, pc, s);
+    else launch_dq_t4<DQK, DV, false, false>(d, qc, kc, ks, vc, doc, lse, delta, dq, ps, pa, pc, s);
   }
 }
 
 // dQ launcher for d_qk = 192, d_v = 128, compiled in its own translation unit
 // (attn_dq_wide.hip) with the compiler's default MFMA register form.
 hipError_t launch_dq_192_128(const AttnDims& d, Operand qc, Operand kc, Operand ks, Operand vc, Operand doc,
-                             const float* lse, const float* delta, float* dq, double* ps, double* pa, hipStream_t s);
+                             const float* lse, const float* delta, float* dq, double* ps, double* pa, double* pc,
+                             hipStream_t s);
 
 }  // namespace dm

@@ -4,8 +4,9 @@
 namespace dm {
 
 hipError_t launch_dq_192_128(const AttnDims& d, Operand qc, Operand kc, Operand ks, Operand vc, Operand doc,
-                             const float* lse, const float* delta, float* dq, double* ps, double* pa, hipStream_t s) {
-  launch_dq_t<192, 128>(d, qc, kc, ks, vc, doc, lse, delta, dq, ps, pa, s);
+                             const float* lse, const float* delta, float* dq, double* ps, double* pa, double* pc,
+                             hipStream_t s) {
+  launch_dq_t<192, 128>(d, qc, kc, ks, vc, doc, lse, delta, dq, ps, pa, pc, s);
   return hipGetLastError();
 }
 

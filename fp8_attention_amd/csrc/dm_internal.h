@@ -38,8 +38,11 @@ hipError_t launch_dkdv(const AttnDims& d, Operand qc, Operand qs, Operand kc, Op
 hipError_t launch_dkdv_d128(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand vc, Operand doc,
                             Operand dos, const float* lse, const float* delta, float* dk, float* dv, hipStream_t s);
 
+// ps, pa, pc: the row-sum probes (pre-cast sum of dS, sum of |P dP^|, sum of the
+// decoded dS^<k>); ps and pa both null or both set, pc only with them
 hipError_t launch_dq(const AttnDims& d, Operand qc, Operand kc, Operand ks, Operand vc, Operand doc,
-                     const float* lse, const float* delta, float* dq, double* ps, double* pa, hipStream_t s);
+                     const float* lse, const float* delta, float* dq, double* ps, double* pa, double* pc,
+                     hipStream_t s);
 
 hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t s);
 

@@ -179,6 +179,25 @@ dm_status dm_attn_bwd_dq(const dm_attn_shape* shape, dm_fp8_operand q_c, dm_fp8_
                          const float* lse, const float* delta, float* dq,
                          double* probe_rowsum_ds, double* probe_rowsum_abs_pdp, hipStream_t stream);
 
+/*
+ * dm_attn_bwd_dq with a third row-sum probe (section 03 "Does matching the
+ * backward operands fix it?": Delta-Matching makes the row sums of dS vanish up
+ * to FP32 rounding before dS is cast to FP8, and the cast then adds a row-sum
+ * residual of its own, which the page compares between stale delta and
+ * Delta-Matching):
+ *   probe_rowsum_ds, probe_rowsum_abs_pdp: as for dm_attn_bwd_dq;
+ *   probe_rowsum_ds_cast: [B][Hq][L] double, sum_j dS^<k>_ij, the dS that enters
+ *   the dQ product after its E5M2 cast in 32-key blocks (decoded codes times the
+ *   block scales), summed in FP32 per 128 keys and FP64 across them.
+ * dq as for dm_attn_bwd_dq.  All three probe pointers are required (non-NULL,
+ * 16-byte aligned); other errors as for dm_attn_bwd.
+ */
+dm_status dm_attn_bwd_dq_probes(const dm_attn_shape* shape, dm_fp8_operand q_c, dm_fp8_operand k_c,
+                                dm_fp8_operand k_s, dm_fp8_operand v_c, dm_fp8_operand do_c,
+                                const float* lse, const float* delta, float* dq,
+                                double* probe_rowsum_ds, double* probe_rowsum_abs_pdp,
+                                double* probe_rowsum_ds_cast, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -252,16 +252,20 @@ def _pad_rows(x, n32):
 
 
 def backward_rows(ops_h, lse, delta, sigma, causal, r0, r1, cast=True, radius=False,
-                  delta_err=None, lse_err=None):
+                  delta_err=None, lse_err=None, keep_ds=False):
     """Backward for query rows [r0, r1) of one head (r0 % 32 == 0; r1 % 32 == 0 or r1 == L).
 
     ``ops_h`` holds the decoded operands of this head: q_c, k_c, v_c, do_c,
     q_s, k_s, do_s as [L, d].  Returns dQ for the rows, and the partial dK, dV
-    contributed by these rows (sum them over row ranges and the heads of a group).
-    With ``radius`` also the flip radii r_* and accumulation bounds b_* of dq,
-    dk, dv, and b_rowsum.  ``delta_err`` / ``lse_err`` bound how far the delta
-    and LSE the kernel is given may sit from the exact ones (default: float32
-    rounding).
+    contributed by these rows (sum them over row ranges and the heads of a group),
+    and per row: the sum of dS before its casts ("rowsum"), of |P dP_hat|
+    ("rowabs") and of dS^<k> after its E5M2 cast along keys ("rowsum_cast": the
+    residual the cast adds once Delta-Matching has removed the pre-cast one,
+    project page section 03).  With ``radius`` also the flip radii r_* and
+    accumulation bounds b_* of dq, dk, dv, b_rowsum, and r_/b_rowsum_cast.
+    ``delta_err`` / ``lse_err`` bound how far the delta and LSE the kernel is
+    given may sit from the exact ones (default: float32 rounding).  ``keep_ds``
+    also returns the pre-cast dS of the rows ("ds").
     """
     Q, K, Vc = ops_h["q_c"], ops_h["k_c"], ops_h["v_c"]
     dOc, Qs, Ks, dOs = ops_h["do_c"], ops_h["q_s"], ops_h["k_s"], ops_h["do_s"]
@@ -311,6 +315,7 @@ def backward_rows(ops_h, lse, delta, sigma, causal, r0, r1, cast=True, radius=Fa
         "dv": Pq[:, :L].T @ dOs[r0:r1],
         "rowsum": rowsum,
         "rowabs": rowabs,
+        "rowsum_cast": dSk[:, :L].sum(axis=1),
         "n_flag": flags[0],
         "n_block_flag": flags[1],
     }
@@ -323,6 +328,10 @@ def backward_rows(ops_h, lse, delta, sigma, causal, r0, r1, cast=True, radius=Fa
         out["b_dk"] = GAMMA * abs(sigma) * (np.abs(dSq[:, :L]).T @ aQ)
         out["b_dv"] = GAMMA * (np.abs(Pq[:, :L]).T @ aO)
         out["b_rowsum"] = b_rowsum
+        out["r_rowsum_cast"] = ddSk[:, :L].sum(axis=1)
+        out["b_rowsum_cast"] = TAU * np.abs(dSk[:, :L]).sum(axis=1)
+    if keep_ds:
+        out["ds"] = dS[:, :L]
     return out
 
 
@@ -468,11 +477,13 @@ def backward(ops: dict, shp: Shape, lse, delt, rows=None, cast=True, radius=Fals
     dV = np.zeros((B, Hkv, L, shp.d_v))
     rs = np.full((B, Hq, L), np.nan)
     ra = np.full((B, Hq, L), np.nan)
+    rc = np.full((B, Hq, L), np.nan)
     ext = {}
     if radius:
         ext = {"r_dq": np.full_like(dQ, np.nan), "b_dq": np.full_like(dQ, np.nan),
                "r_dk": np.zeros_like(dK), "b_dk": np.zeros_like(dK),
-               "r_dv": np.zeros_like(dV), "b_dv": np.zeros_like(dV), "b_rowsum": np.full_like(rs, np.nan)}
+               "r_dv": np.zeros_like(dV), "b_dv": np.zeros_like(dV), "b_rowsum": np.full_like(rs, np.nan),
+               "r_rowsum_cast": np.full_like(rs, np.nan), "b_rowsum_cast": np.full_like(rs, np.nan)}
     nflag = nblock = 0
     for b in range(B):
         for h in range(Hq):
@@ -490,13 +501,16 @@ def backward(ops: dict, shp: Shape, lse, delt, rows=None, cast=True, radius=Fals
                 dV[b, g] += r["dv"]
                 rs[b, h, r0:r1] = r["rowsum"]
                 ra[b, h, r0:r1] = r["rowabs"]
+                rc[b, h, r0:r1] = r["rowsum_cast"]
                 nflag += r["n_flag"]
                 nblock += r["n_block_flag"]
                 if radius:
                     ext["r_dq"][b, h, r0:r1] = r["r_dq"]
                     ext["b_dq"][b, h, r0:r1] = r["b_dq"]
                     ext["b_rowsum"][b, h, r0:r1] = r["b_rowsum"]
+                    ext["r_rowsum_cast"][b, h, r0:r1] = r["r_rowsum_cast"]
+                    ext["b_rowsum_cast"][b, h, r0:r1] = r["b_rowsum_cast"]
                     for k in ("r_dk", "b_dk", "r_dv", "b_dv"):
                         ext[k][b, g] += r[k]
-    return {"dq": dQ, "dk": dK, "dv": dV, "rowsum": rs, "rowabs": ra,
+    return {"dq": dQ, "dk": dK, "dv": dV, "rowsum": rs, "rowabs": ra, "rowsum_cast": rc,
             "n_flag": nflag, "n_block_flag": nblock, **ext}

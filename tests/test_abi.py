@@ -124,7 +124,13 @@ def test_split_backward_validation():
     assert lib.dm_attn_bwd_dkdv(ctypes.byref(s), *[op] * 6, FAKE, FAKE, FAKE, MIS, None) == _lib.DM_ERR_ALIGN
     assert lib.dm_attn_bwd_dq(ctypes.byref(s), *[op] * 5, FAKE, FAKE, FAKE, FAKE, None, None) == _lib.DM_ERR_NULL
     assert lib.dm_attn_bwd_dq(ctypes.byref(s), *[op] * 5, FAKE, FAKE, MIS, None, None, None) == _lib.DM_ERR_ALIGN
+    # the three-probe dQ call requires every probe buffer
+    pr = lib.dm_attn_bwd_dq_probes
+    assert pr(ctypes.byref(s), *[op] * 5, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == _lib.DM_ERR_NULL
+    assert pr(ctypes.byref(s), *[op] * 5, FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == _lib.DM_ERR_NULL
+    assert pr(ctypes.byref(s), *[op] * 5, FAKE, FAKE, FAKE, FAKE, FAKE, MIS, None) == _lib.DM_ERR_ALIGN
     s.d_qk = 96
+    assert pr(ctypes.byref(s), *[op] * 5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == _lib.DM_ERR_SHAPE
     assert lib.dm_attn_bwd_dkdv(ctypes.byref(s), *[op] * 6, FAKE, FAKE, FAKE, FAKE, None) == _lib.DM_ERR_SHAPE
     assert lib.dm_attn_bwd_dq(ctypes.byref(s), *[op] * 5, FAKE, FAKE, FAKE, None, None, None) == _lib.DM_ERR_SHAPE
 

@@ -137,3 +137,36 @@ def test_fullsize_chain_sampled(name):
         t = dk if n == "dk" else dv
         _log("   ", U.compare(n, t[ksl], r[n], allow=r["r_" + n] + r["b_" + n], norm_rel=U.NORM_TOL,
                               mask=np.broadcast_to(keys, r[n].shape)))
+
+
+@pytest.mark.parametrize("name", ["gqa_4k", "gqa_8k"])
+def test_postcast_rowsum_residual_stale_vs_matched(name):
+    """Direction of the project page's kernel probe (section 03): after dS is cast to FP8,
+    the normalized row-sum residual |sum_j dS^<k>_ij| / sum_j |P_ij dP^_ij| is larger with
+    the stale correction than with Delta-Matching (the page reports 5.3-6.3x on its
+    models' activations; these synthetic inputs only fix the sign of the comparison).
+    Both corrections start from the same GPU forward; the stale one from the bf16 dO."""
+    from fp8_attention_amd import api
+    w = W.WORKLOADS[name]
+    inputs = W.generate(w)
+    dev = {n: t.cuda() for n, t in inputs.items()}
+    shape = api.AttnShape(w.batch, w.heads_q, w.heads_kv, w.seqlen, w.d_qk, w.d_v, w.causal)
+    ops = api.quantize_operands(dev["q"], dev["k"], dev["v"], dev["do"])
+    o, lse = api.attn_fwd(shape, ops["q_c"], ops["k_c"], ops["v_s"])
+    res = {}
+    for mode in ("stale", "matched"):
+        if mode == "stale":
+            d = api.attn_delta(shape, mode, o=o, do=dev["do"])
+        else:
+            d = api.attn_delta(shape, mode, do_c=ops["do_c"], q_c=ops["q_c"], k_c=ops["k_c"], v_c=ops["v_c"],
+                               lse=lse)
+        p = api.attn_bwd_dq(shape, ops, lse, d, probe_cast=True)
+        torch.cuda.synchronize()
+        ra = U.to64(p["rowabs"])
+        res[mode] = (np.abs(U.to64(p["rowsum"])) / ra, np.abs(U.to64(p["rowsum_cast"])) / ra)
+    pre = np.mean(res["stale"][0]) / np.mean(res["matched"][0])
+    post = np.mean(res["stale"][1]) / np.mean(res["matched"][1])
+    _log(f"   {name}: mean normalized row-sum residual stale/matched: before the cast {pre:.1f}x "
+         f"(matched {np.mean(res['matched'][0]):.2e}), after the cast {post:.2f}x "
+         f"(stale {np.mean(res['stale'][1]):.3e}, matched {np.mean(res['matched'][1]):.3e})")
+    assert post > 1.0

@@ -203,6 +203,13 @@ def test_chain_matched_rowsums_and_parity(name):
         _log("   ", U.compare(n, g[n], b[n], allow=b["r_" + n] + b["b_" + n], norm_rel=U.NORM_TOL))
     rs, ra = U.to64(g["rowsum"]), U.to64(g["rowabs"])
     assert np.all(np.abs(rs) <= U.ROWSUM_TOL * ra), float(np.max(np.abs(rs) / np.maximum(ra, 1e-300)))
+    # the row sums after the E5M2 cast along keys (the third probe)
+    api = _api()
+    pc = api.attn_bwd_dq(shape, ops, g["lse"], g["delta"], probe_cast=True)
+    torch.cuda.synchronize()
+    assert torch.equal(pc["dq"], g["dq"]) and torch.equal(pc["rowsum"], g["rowsum"])
+    U.compare("rowsum_cast", pc["rowsum_cast"], b["rowsum_cast"],
+              allow=b["r_rowsum_cast"] + b["b_rowsum_cast"] + 1e-30, rel=0.0)
 
 
 @pytest.mark.parametrize("mode", ["stale", "do_matched"])

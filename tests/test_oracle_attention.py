@@ -336,3 +336,34 @@ def test_quantized_layouts_brute_force():
     assert not c[0, :, :, 70:].any()
     back = A.dequantize_sequence(c, s, "e5m2", 70)
     assert back.shape == x.shape and np.abs(back - x).max() < 0.2 * np.abs(x).max()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_postcast_rowsum_is_the_sum_of_the_e5m2_cast(causal):
+    """rowsum_cast is sum_j of dS cast to E5M2 in 32-key blocks: recomputed here from the
+    oracle's pre-cast dS through torch's float8_e5m2 cast, with each block's scale taken
+    from its definition (smallest power of two 2^k with amax <= 57344 * 2^k)."""
+    rng = np.random.default_rng(21)
+    B, Hq, Hkv, L, d = 1, 1, 1, 200, 64
+    q, k, v, do, ops = _rand_ops(rng, B, Hq, Hkv, L, d, d)
+    shp = _shape(B, Hq, Hkv, L, d, d, causal)
+    f = A.forward(ops, shp)
+    dm = A.delta(ops, shp, "matched", lse=f["lse"])
+    oh = {n: ops[n][0, 0] for n in ("q_c", "k_c", "v_c", "do_c", "q_s", "k_s", "do_s")}
+    r = A.backward_rows(oh, f["lse"][0, 0], dm[0, 0], shp.sigma, causal, 0, L, keep_ds=True)
+    ds = np.zeros((L, 224))
+    ds[:, :L] = r["ds"]
+    blocks = ds.reshape(L, 7, 32)
+    amax = np.abs(blocks).max(axis=-1)
+    kexp = np.where(amax > 0, np.ceil(np.log2(np.maximum(amax, 1e-300) / 57344.0)), -126).clip(-126, 127)
+    # ceil(log2(.)) can land one above the minimum when the ratio is an exact power of two
+    kexp = np.where((amax > 0) & (amax <= 57344.0 * np.exp2(kexp - 1)), kexp - 1, kexp)
+    scale = np.exp2(kexp)[..., None]
+    cast = torch.from_numpy(blocks / scale).to(torch.float8_e5m2).to(torch.float64).numpy() * scale
+    want = cast.reshape(L, 224)[:, :L].sum(axis=1)
+    assert np.allclose(r["rowsum_cast"], want, rtol=1e-12, atol=1e-300)
+    # without the cast the post-cast sum is the pre-cast one; with matched delta that is ~0
+    u = A.backward_rows(oh, f["lse"][0, 0], dm[0, 0], shp.sigma, causal, 0, L, cast=False)
+    assert np.all(np.abs(u["rowsum_cast"] - u["rowsum"]) <= 1e-14 * u["rowabs"])
+    assert np.all(np.abs(r["rowsum"]) <= 1e-12 * r["rowabs"])
+    assert np.median(np.abs(r["rowsum_cast"]) / r["rowabs"]) > 1e-6   # the cast leaves a residual
