@@ -11,8 +11,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdm.so")
-SOURCES = ["api.hip", "quantize.hip", "attn_fwd.hip", "attn_delta.hip", "attn_bwd.hip", "attn_dq.hip",
-           "attn_dq_wide.hip", "attn_dkdv128.hip"]
+SOURCES = ["api.hip", "quantize.hip", "attn_fwd.hip", "attn_delta.hip", "attn_bwd.hip", "attn_dkdv_wide.hip",
+           "attn_dq.hip", "attn_dq_wide.hip", "attn_dkdv128.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # keep the compiler away from packed FP32 instructions on this target
@@ -23,11 +23,12 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 # Attention kernels: scores are finite or -inf by construction, so max
 # reductions need no NaN canonicalisation (this lets them map onto v_max3_f32).
 EXTRA = {src: ["-fno-honor-nans"]
-         for src in ("attn_fwd.hip", "attn_delta.hip", "attn_bwd.hip", "attn_dq.hip", "attn_dq_wide.hip",
-                     "attn_dkdv128.hip")}
+         for src in ("attn_fwd.hip", "attn_delta.hip", "attn_bwd.hip", "attn_dkdv_wide.hip", "attn_dq.hip",
+                     "attn_dq_wide.hip", "attn_dkdv128.hip")}
 # The generic dK/dV kernel and the dQ kernels: keep MFMA results in VGPRs so the FP32
 # softmax work on the score tiles does not shuttle them through AGPRs.  (The
-# d_qk=192/d_v=128 dQ instance is built without it: the compiler fails on it.)
+# d_qk=192/d_v=128 dQ instance is built without it: the compiler fails on it; the
+# d = 256 instances, one wave per SIMD, need the AGPRs for their accumulators.)
 EXTRA["attn_bwd.hip"] += ["-mllvm", "--amdgpu-mfma-vgpr-form"]
 EXTRA["attn_dq.hip"] += ["-mllvm", "--amdgpu-mfma-vgpr-form"]
 

@@ -17,8 +17,10 @@ dm_status check_shape(const dm_attn_shape* s) {
   if (s->heads_q % s->heads_kv != 0) return DM_ERR_SHAPE;
   // every kernel grid is one-dimensional over (sequence tile of 128, head, batch)
   if ((int64_t)s->batch * s->heads_q * ((s->seqlen + 127) / 128) > INT32_MAX) return DM_ERR_SHAPE;
-  if (s->d_qk != 64 && s->d_qk != 128 && s->d_qk != 192) return DM_ERR_SHAPE;
-  if (s->d_v != 64 && s->d_v != 128) return DM_ERR_SHAPE;
+  // d_qk in {64, 128, 192} with d_v in {64, 128}, or d_qk = d_v = 256
+  const bool wide = s->d_qk == 256 && s->d_v == 256;
+  if (!wide && s->d_qk != 64 && s->d_qk != 128 && s->d_qk != 192) return DM_ERR_SHAPE;
+  if (!wide && s->d_v != 64 && s->d_v != 128) return DM_ERR_SHAPE;
   if (s->causal != 0 && s->causal != 1) return DM_ERR_SHAPE;
   if (!(s->softmax_scale > 0.f) || !isfinite(s->softmax_scale)) return DM_ERR_SHAPE;
   return DM_OK;

@@ -77,7 +77,10 @@ hipError_t launch_delta_rows(const AttnDims& d, int mode, const float* o, const 
   int64_t blocks = (nrows + rpb - 1) / rpb;
   if (blocks > 256 * 32) blocks = 256 * 32;
   const bool m = mode == 1;
-  if (d.dv == 128) {
+  if (d.dv == 256) {
+    if (m) hipLaunchKernelGGL((delta_rows_kernel<256, true>), dim3(blocks), dim3(256), 0, s, o, dob, doc.codes, doc.scales, delta, nrows, d.L, d.Lp);
+    else hipLaunchKernelGGL((delta_rows_kernel<256, false>), dim3(blocks), dim3(256), 0, s, o, dob, doc.codes, doc.scales, delta, nrows, d.L, d.Lp);
+  } else if (d.dv == 128) {
     if (m) hipLaunchKernelGGL((delta_rows_kernel<128, true>), dim3(blocks), dim3(256), 0, s, o, dob, doc.codes, doc.scales, delta, nrows, d.L, d.Lp);
     else hipLaunchKernelGGL((delta_rows_kernel<128, false>), dim3(blocks), dim3(256), 0, s, o, dob, doc.codes, doc.scales, delta, nrows, d.L, d.Lp);
   } else {
@@ -90,34 +93,38 @@ hipError_t launch_delta_rows(const AttnDims& d, int mode, const float* o, const 
 // ---------------------------------------------------------------------------
 // matched
 // ---------------------------------------------------------------------------
-constexpr int kDelWaves = 8;
-constexpr int kDelQ = 32 * kDelWaves;    // queries per workgroup
+// waves per workgroup (32 queries each): two per SIMD; one per SIMD when
+// d_qk = d_v = 256, whose Q, dO rows and score tiles fill more than half the file
+template <int DQK, int DV> constexpr int delta_waves() { return DQK + DV > 384 ? 4 : 8; }
 
 template <int DQK, int DV>
 struct DeltaLds {
+  static constexpr int NW = delta_waves<DQK, DV>();
   static constexpr int KB = DQK / 32, VB = DV / 32;
   static constexpr int K = kChunk * DQK, V = kChunk * DV;      // K^<c>, V^<c> rows of a chunk, swizzled
   static constexpr int KS = kChunk * KB * 4, VS = kChunk * VB * 4;
   static constexpr int BUF = K + V + KS + VS;                  // one chunk
   static constexpr int OFF_V = K, OFF_KS = K + V, OFF_VS = K + V + KS;
   static constexpr int NJ = BUF / 1024;                        // direct loads per chunk
-  static constexpr int NJW = (NJ + kDelWaves - 1) / kDelWaves;
+  static constexpr int NJW = (NJ + NW - 1) / NW;
   static_assert(K % 1024 == 0 && V % 1024 == 0 && KS % 1024 == 0 && VS % 1024 == 0, "whole 1 KB loads");
+  static_assert(2 * BUF <= 160 * 1024, "LDS budget");
 };
 
-// Workgroup = 8 waves = 256 queries; 1-D grid over (query tile, Hq, B), query
+// Workgroup = 8 waves = 256 queries (4 waves = 128 when d = 256); 1-D grid over (query tile, Hq, B), query
 // tile slowest and the longest causal tiles first.  Per 128-key chunk and 32-key tile:
 // S^T = K Q^T and dP^T = V dO^T (lane pair = query, 16 keys per lane), then
 // delta += sum P * dP^ with P = exp2(S sigma log2e - LSE log2e).  The tiles of
 // chunk c+1 are computed as soon as tile t of chunk c has been consumed; K^<c> /
 // V^<c> chunks are double-buffered in LDS via direct global->LDS loads.
 template <int DQK, int DV, bool CAUSAL>
-__global__ __launch_bounds__(64 * kDelWaves) void delta_matched_kernel(
+__global__ __launch_bounds__((64 * delta_waves<DQK, DV>())) void delta_matched_kernel(
     const uint8_t* __restrict__ qc, const float* __restrict__ qcs, const uint8_t* __restrict__ kc,
     const float* __restrict__ kcs, const uint8_t* __restrict__ vc, const float* __restrict__ vcs,
     const uint8_t* __restrict__ doc, const float* __restrict__ docs, const float* __restrict__ lse,
     float* __restrict__ delta, int Hq, int Hkv, int L, int Lp, float sigma) {
   using C = DeltaLds<DQK, DV>;
+  constexpr int kDelWaves = C::NW, kDelQ = 32 * kDelWaves;
   constexpr int KS = DQK / 64, VS = DV / 64;
   constexpr int KB = DQK / 32, VB = DV / 32;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::BUF];
@@ -288,13 +295,14 @@ __global__ __launch_bounds__(64 * kDelWaves) void delta_matched_kernel(
 template <int DQK, int DV>
 static void launch_dm_t(const AttnDims& d, Operand doc, Operand q, Operand k, Operand v, const float* lse,
                         float* delta, hipStream_t s) {
-  dim3 grid((unsigned)((d.Lp + kDelQ - 1) / kDelQ) * d.Hq * d.B);
+  constexpr int NW = delta_waves<DQK, DV>();
+  dim3 grid((unsigned)((d.Lp + 32 * NW - 1) / (32 * NW)) * d.Hq * d.B);
   if (d.causal)
-    hipLaunchKernelGGL((delta_matched_kernel<DQK, DV, true>), grid, dim3(64 * kDelWaves), 0, s, q.codes, q.scales,
+    hipLaunchKernelGGL((delta_matched_kernel<DQK, DV, true>), grid, dim3(64 * NW), 0, s, q.codes, q.scales,
                        k.codes, k.scales, v.codes, v.scales, doc.codes, doc.scales, lse, delta, d.Hq, d.Hkv, d.L,
                        d.Lp, d.sigma);
   else
-    hipLaunchKernelGGL((delta_matched_kernel<DQK, DV, false>), grid, dim3(64 * kDelWaves), 0, s, q.codes, q.scales,
+    hipLaunchKernelGGL((delta_matched_kernel<DQK, DV, false>), grid, dim3(64 * NW), 0, s, q.codes, q.scales,
                        k.codes, k.scales, v.codes, v.scales, doc.codes, doc.scales, lse, delta, d.Hq, d.Hkv, d.L,
                        d.Lp, d.sigma);
 }
@@ -307,6 +315,7 @@ hipError_t launch_delta_matched(const AttnDims& d, Operand doc, Operand q, Opera
   else if (d.dqk == 64 && d.dv == 128) launch_dm_t<64, 128>(d, doc, q, k, v, lse, delta, s);
   else if (d.dqk == 128 && d.dv == 64) launch_dm_t<128, 64>(d, doc, q, k, v, lse, delta, s);
   else if (d.dqk == 192 && d.dv == 64) launch_dm_t<192, 64>(d, doc, q, k, v, lse, delta, s);
+  else if (d.dqk == 256 && d.dv == 256) launch_dm_t<256, 256>(d, doc, q, k, v, lse, delta, s);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -1,11 +1,13 @@
 // dQ of block-scaled FP8 attention (query-stationary), with the row-sum probes.
 //
-// Workgroup = 8 waves = 256 queries (32 per wave; 4 waves when the probes are on);
+// Workgroup = 8 waves = 256 queries (32 per wave; 4 waves when the probes are on
+// or d_qk = d_v = 256);
 // a 1-D grid over (query tile, Hq, B) with the query tile slowest, so the longest
 // causal tiles start first.
 // The wave's Q^<c> and dO^<c> rows sit in registers as the B operands of
 // S^T = K Q^T and dP^T = V dO^T, so both score tiles come out with one query per
-// lane pair and 16 keys per lane.  Per 128-key chunk and 32-key tile:
+// lane pair and 16 keys per lane.  Per 128-key chunk (64 keys when d = 256) and
+// 32-key tile:
 // P = exp(S - LSE), dS = P (dP^ - delta) in FP32; dS is cast to E5M2 in 32-key
 // blocks in registers (the lane pair holds a whole block) and is already the B
 // operand of dQ^T += K^<s>^T dS^<k>^T.  Each dQ row is written once, so dQ needs
@@ -22,16 +24,21 @@
 namespace dm {
 
 // waves per workgroup (32 queries each): 8 (two per SIMD); the probe variant, with
-// its extra row sums live, runs one wave per SIMD with the full register file
-template <bool PROBE> constexpr int dq_waves() { return PROBE ? 4 : 8; }
+// its extra row sums live, and d_qk = d_v = 256, with 256-channel dQ accumulators,
+// run one wave per SIMD with the full register file
+template <bool PROBE, int DQK, int DV> constexpr int dq_waves() { return (PROBE || DQK + DV > 384) ? 4 : 8; }
+// keys per LDS chunk: 128, or 64 when d_qk = d_v = 256 (two chunks of K^<c>, V^<c>
+// and K^<s> at 128 keys would not fit in LDS)
+template <int DQK, int DV> constexpr int dq_chunk() { return DQK + DV > 384 ? 64 : 128; }
 
-template <int DQK, int DV, int NW>
+template <int DQK, int DV, int NW, int CK>
 struct DqLds {
   static constexpr int KB = DQK / 32, VB = DV / 32;
-  // K part: K^<c> rows [128][DQK] (swizzled) + scales [128][KB]
-  static constexpr int K = kChunk * DQK, KS = kChunk * KB * 4, KPART = K + KS;
-  // V part: V^<c> rows [128][DV] + scales [128][VB], K^<s> rows [DQK][128] + scales [DQK][4]
-  static constexpr int V = kChunk * DV, VS = kChunk * VB * 4, T = DQK * kChunk, TS = DQK * 16;
+  // K part: K^<c> rows [CK][DQK] (swizzled) + scales [CK][KB]
+  static constexpr int K = CK * DQK, KS = CK * KB * 4, KPART = K + KS;
+  // V part: V^<c> rows [CK][DV] + scales [CK][VB], K^<s> rows [DQK][CK] + scales [DQK][4]
+  // (the aligned group of four 32-key blocks that holds the chunk's blocks)
+  static constexpr int V = CK * DV, VS = CK * VB * 4, T = DQK * CK, TS = DQK * 16;
   static constexpr int OFF_VS = V, OFF_T = V + VS, OFF_TS = V + VS + T, VPART = V + VS + T + TS;
   static constexpr int OFF_VP = 2 * KPART;                      // V parts follow the two K parts
   static constexpr int BYTES = 2 * KPART + 2 * VPART;
@@ -39,10 +46,11 @@ struct DqLds {
   static constexpr int NJKW = (NJK + NW - 1) / NW, NJVW = (NJV + NW - 1) / NW;
   static_assert(K % 1024 == 0 && KS % 1024 == 0 && V % 1024 == 0 && VS % 1024 == 0 && T % 1024 == 0 &&
                 TS % 1024 == 0, "whole 1 KB loads");
+  static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
 template <int DQK, int DV, bool CAUSAL, bool PROBE>
-__global__ __launch_bounds__(64 * dq_waves<PROBE>()) void dq_kernel(
+__global__ __launch_bounds__((64 * dq_waves<PROBE, DQK, DV>())) void dq_kernel(
     const uint8_t* __restrict__ qc, const float* __restrict__ qcs, const uint8_t* __restrict__ kc,
     const float* __restrict__ kcs, const uint8_t* __restrict__ vc, const float* __restrict__ vcs,
     const uint8_t* __restrict__ kst, const float* __restrict__ ksts, const uint8_t* __restrict__ doc,
@@ -50,8 +58,9 @@ __global__ __launch_bounds__(64 * dq_waves<PROBE>()) void dq_kernel(
     float* __restrict__ dq, double* __restrict__ psum, double* __restrict__ pabs, double* __restrict__ pcast, int Hq,
     int Hkv, int L, int Lp,
     float sigma) {
-  constexpr int kDqWaves = dq_waves<PROBE>(), kDqQ = 32 * kDqWaves;
-  using C = DqLds<DQK, DV, kDqWaves>;
+  constexpr int kDqWaves = dq_waves<PROBE, DQK, DV>(), kDqQ = 32 * kDqWaves;
+  constexpr int CK = dq_chunk<DQK, DV>(), NTL = CK / 32, NST = CK / 64;   // key tiles, 64-key halves
+  using C = DqLds<DQK, DV, kDqWaves, CK>;
   constexpr int KS = DQK / 64, VS = DV / 64, KB = DQK / 32, VB = DV / 32;
   constexpr int NCT = DQK / 32;                 // 32-channel tiles of dQ^T
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::BYTES];
@@ -99,8 +108,8 @@ __global__ __launch_bounds__(64 * dq_waves<PROBE>()) void dq_kernel(
     } else if (pb < C::OFF_T) {
       off = pb - C::OFF_VS;
     } else if (pb < C::OFF_TS) {
-      const int p = pb - C::OFF_T, r = p / kChunk;          // 8 channel rows of 128 B per load
-      off = (lane >> 3) * Lp + 16 * tile_slot<kChunk>(r, lane & 7);
+      const int p = pb - C::OFF_T, r = p / CK;              // 1024 / CK channel rows of CK B per load
+      off = (lane / (CK / 16)) * Lp + 16 * tile_slot<CK>(r, lane % (CK / 16));
     } else {
       off = lane * LB * 4;                                  // channel 64j + lane, 16 B (4 key blocks)
     }
@@ -112,8 +121,8 @@ __global__ __launch_bounds__(64 * dq_waves<PROBE>()) void dq_kernel(
       const int j = w + kDqWaves * i;
       if (j >= C::NJK) continue;
       const int jb = j * 1024;
-      const uint8_t* base = jb < C::K ? Kc + (int64_t)cc * kChunk * DQK
-                                      : reinterpret_cast<const uint8_t*>(Kcs + (int64_t)cc * kChunk * KB);
+      const uint8_t* base = jb < C::K ? Kc + (int64_t)cc * CK * DQK
+                                      : reinterpret_cast<const uint8_t*>(Kcs + (int64_t)cc * CK * KB);
       dma16(base + ko[i], lds + buf * C::KPART + jb);
     }
   };
@@ -124,10 +133,11 @@ __global__ __launch_bounds__(64 * dq_waves<PROBE>()) void dq_kernel(
       if (j >= C::NJV) continue;
       const int jb = j * 1024;
       const uint8_t* base;
-      if (jb < C::OFF_VS) base = Vc + (int64_t)cc * kChunk * DV;
-      else if (jb < C::OFF_T) base = reinterpret_cast<const uint8_t*>(Vcs + (int64_t)cc * kChunk * VB);
-      else if (jb < C::OFF_TS) base = Kt + (int64_t)((jb - C::OFF_T) / kChunk) * Lp + cc * kChunk;
-      else base = reinterpret_cast<const uint8_t*>(Kts + (int64_t)(64 * ((jb - C::OFF_TS) / 1024)) * LB + cc * 4);
+      if (jb < C::OFF_VS) base = Vc + (int64_t)cc * CK * DV;
+      else if (jb < C::OFF_T) base = reinterpret_cast<const uint8_t*>(Vcs + (int64_t)cc * CK * VB);
+      else if (jb < C::OFF_TS) base = Kt + (int64_t)((jb - C::OFF_T) / CK) * Lp + cc * CK;
+      else base = reinterpret_cast<const uint8_t*>(Kts + (int64_t)(64 * ((jb - C::OFF_TS) / 1024)) * LB +
+                                                   ((cc * (CK / kBlock)) & ~3));
       dma16(base + vo[i], lds + C::OFF_VP + buf * C::VPART + jb);
     }
   };
@@ -157,7 +167,7 @@ __global__ __launch_bounds__(64 * dq_waves<PROBE>()) void dq_kernel(
     }
   }
   const int kr = pair_row(R);
-  int kro[KS][2], vro[VS][2], tro[2][2];
+  int kro[KS][2], vro[VS][2], tro[NST][2];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -167,9 +177,9 @@ __global__ __launch_bounds__(64 * dq_waves<PROBE>()) void dq_kernel(
 #pragma unroll
     for (int e = 0; e < 2; ++e) vro[ks][e] = kr * DV + 16 * tile_slot<DV>(kr, 4 * ks + 2 * e + h);
 #pragma unroll
-  for (int st = 0; st < 2; ++st)
+  for (int st = 0; st < NST; ++st)
 #pragma unroll
-    for (int e = 0; e < 2; ++e) tro[st][e] = R * kChunk + 16 * tile_slot<kChunk>(R, 4 * st + 2 * e + h);
+    for (int e = 0; e < 2; ++e) tro[st][e] = R * CK + 16 * tile_slot<CK>(R, 4 * st + 2 * e + h);
 
   const float c2 = sigma * kLog2e;
   const float l2 = (live && qi < L) ? lse[qhead * L + qi] * kLog2e : INFINITY;   // pad rows: P = 0
@@ -181,8 +191,8 @@ __global__ __launch_bounds__(64 * dq_waves<PROBE>()) void dq_kernel(
 
   const int kmax = CAUSAL ? min(qi, L - 1) : L - 1;       // last key this lane's query sees
   const int qlast = min(q0 + kDqQ, Lp) - 1;
-  const int nchunks = CAUSAL ? (qlast / kChunk + 1) : Lp / kChunk;
-  const int wlast = CAUSAL ? min(nchunks - 1, (qw + 31) / kChunk) : nchunks - 1;
+  const int nchunks = CAUSAL ? (qlast / CK + 1) : Lp / CK;
+  const int wlast = CAUSAL ? min(nchunks - 1, (qw + 31) / CK) : nchunks - 1;
 
   auto score_tile = [&](int buf, int t) -> v16f {
     const uint8_t* bb = lds + buf * C::KPART;
@@ -200,14 +210,15 @@ __global__ __launch_bounds__(64 * dq_waves<PROBE>()) void dq_kernel(
   // one chunk of work for this wave; MASK instantiates the causal / ragged mask
   auto chunk = [&](int c, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const int k0 = c * kChunk;
+    const int k0 = c * CK;
     const uint8_t* vp = lds + C::OFF_VP + (c & 1) * C::VPART;
     const float* tsp = reinterpret_cast<const float*>(vp + C::OFF_TS);
-    v8i dsb[2];
-    int dssc[2] = {0, 0};
+    const int tb = (c * (CK / kBlock)) & 3;        // the chunk's first block within the staged four
+    v8i dsb[NST];
+    int dssc[NST] = {};
     float csum = 0.f, cabs = 0.f, ccast = 0.f;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < NTL; ++t) {
       // dP^T tile t of chunk c
       const float* vsr = reinterpret_cast<const float*>(vp + C::OFF_VS) + (32 * t + kr) * VB;
       v16f dp = v16f{};
@@ -254,15 +265,18 @@ __global__ __launch_bounds__(64 * dq_waves<PROBE>()) void dq_kernel(
         }
         ccast += cs * sc;
       }
-      if (t == 1 || t == 3) {
+      if (t & 1) {
         // dS^<k> of key half st complete: dQ^T += K^<s>^T dS^<k>^T over those 64 keys
         const int st = t >> 1;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-          const uint8_t* p = vp + C::OFF_T + 32 * ct * kChunk;
+          const uint8_t* p = vp + C::OFF_T + 32 * ct * CK;
           const v8i a = cat(lds_read16(p + tro[st][0]), lds_read16(p + tro[st][1]));
           const v4f x = *reinterpret_cast<const v4f*>(tsp + (32 * ct + R) * 4);   // 4 key blocks of the channel
-          acc[ct] = mfma<E4M3, E5M2>(a, dsb[st], acc[ct], e8m0(h ? x[2 * st + 1] : x[2 * st]), dssc[st]);
+          float xs;
+          if constexpr (CK == 128) xs = h ? x[2 * st + 1] : x[2 * st];
+          else xs = x[tb + h];
+          acc[ct] = mfma<E4M3, E5M2>(a, dsb[st], acc[ct], e8m0(xs), dssc[st]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);        // one key tile in flight at a time (register budget)
@@ -285,7 +299,7 @@ __global__ __launch_bounds__(64 * dq_waves<PROBE>()) void dq_kernel(
   // Chunks before nfull need no mask for any wave of the workgroup (all their keys
   // precede every query of the tile and lie below L); the rest take the masked body.
   // Two loops keep the mask code out of the main loop's register allocation.
-  const int nfull = min(CAUSAL ? q0 / kChunk : nchunks, L / kChunk);
+  const int nfull = min(CAUSAL ? q0 / CK : nchunks, L / CK);
   issue_k(0, 0);
   issue_v(0, 0);
   int c = 0;
@@ -328,7 +342,7 @@ template <int DQK, int DV, bool CAUSAL, bool PROBE>
 static void launch_dq_t4(const AttnDims& d, Operand qc, Operand kc, Operand ks, Operand vc, Operand doc,
                          const float* lse, const float* delta, float* dq, double* ps, double* pa, double* pc,
                          hipStream_t s) {
-  constexpr int kDqQ = 32 * dq_waves<PROBE>();
+  constexpr int kDqQ = 32 * dq_waves<PROBE, DQK, DV>();
   dim3 grid((unsigned)((d.Lp + kDqQ - 1) / kDqQ) * d.Hq * d.B);
   hipLaunchKernelGGL((dq_kernel<DQK, DV, CAUSAL, PROBE>), grid, dim3(2 * kDqQ), 0, s, qc.codes, qc.scales, kc.codes,
                      kc.scales, vc.codes, vc.scales, ks.codes, ks.scales, doc.codes, doc.scales, lse, delta, dq, ps,
@@ -351,6 +365,10 @@ static void launch_dq_t(const AttnDims& d, Operand qc, Operand kc, Operand ks, O
 // dQ launcher for d_qk = 192, d_v = 128, compiled in its own translation unit
 // (attn_dq_wide.hip) with the compiler's default MFMA register form.
 hipError_t launch_dq_192_128(const AttnDims& d, Operand qc, Operand kc, Operand ks, Operand vc, Operand doc,
+                             const float* lse, const float* delta, float* dq, double* ps, double* pa, double* pc,
+                             hipStream_t s);
+// ... and for d_qk = d_v = 256 (one wave per SIMD: accumulators in AGPRs)
+hipError_t launch_dq_256_256(const AttnDims& d, Operand qc, Operand kc, Operand ks, Operand vc, Operand doc,
                              const float* lse, const float* delta, float* dq, double* ps, double* pa, double* pc,
                              hipStream_t s);
 

@@ -1,6 +1,7 @@
 // Forward of block-scaled FP8 attention on gfx950 matrix cores.
 //
-// Workgroup = 8 waves = 256 queries (32 per wave, 2 waves per SIMD); a 1-D grid
+// Workgroup = 8 waves = 256 queries (32 per wave, 2 waves per SIMD; 4 waves, one
+// per SIMD, when d_v = 256); a 1-D grid
 // over (query tile of 256, Hq, B) with the query tile slowest, so the longest
 // causal tiles are dispatched first.  Each wave keeps its queries' Q^<c> codes in
 // registers as the B operand of S^T = K Q^T, so the score tile comes out with
@@ -28,11 +29,13 @@
 
 namespace dm {
 
-constexpr int kFwdWaves = 8;
-constexpr int kFwdQ = 32 * kFwdWaves;   // queries per workgroup
+// waves per workgroup (32 queries each): two per SIMD; with d_v = 256 the O^T
+// accumulators alone fill half the register file, so one per SIMD
+template <int DQK, int DV> constexpr int fwd_waves() { return DV > 128 ? 4 : 8; }
 
 template <int DQK, int DV>
 struct FwdLds {
+  static constexpr int NW = fwd_waves<DQK, DV>();
   static constexpr int KB = DQK / 32;
   static constexpr int K = kChunk * DQK;               // one K^<c> chunk, rows swizzled
   static constexpr int V = DV * kChunk;                // one V^<s> chunk (channel rows), swizzled
@@ -42,17 +45,18 @@ struct FwdLds {
   static constexpr int BYTES = OFF_VS + 2 * VS;
   // direct-load instructions (1 KB each) per chunk and region
   static constexpr int NK = K / 1024, NV = V / 1024, NKS = KS / 1024, NVS = VS / 1024;
-  static constexpr int NKW = (NK + kFwdWaves - 1) / kFwdWaves, NVW = (NV + kFwdWaves - 1) / kFwdWaves;
+  static constexpr int NKW = (NK + NW - 1) / NW, NVW = (NV + NW - 1) / NW;
   static_assert(K % 1024 == 0 && V % 1024 == 0 && KS % 1024 == 0 && VS % 1024 == 0, "whole 1 KB loads");
-  static_assert(NKS + NVS <= kFwdWaves, "one scale load per wave");
+  static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
 template <int DQK, int DV, bool CAUSAL>
-__global__ __launch_bounds__(64 * kFwdWaves) void fwd_kernel(
+__global__ __launch_bounds__((64 * fwd_waves<DQK, DV>())) void fwd_kernel(
     const uint8_t* __restrict__ qc, const float* __restrict__ qcs, const uint8_t* __restrict__ kc,
     const float* __restrict__ kcs, const uint8_t* __restrict__ vs, const float* __restrict__ vss,
     float* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int L, int Lp, float sigma) {
   using C = FwdLds<DQK, DV>;
+  constexpr int kFwdWaves = C::NW, kFwdQ = 32 * kFwdWaves;
   constexpr int KS = DQK / 64;      // 64-channel steps of QK^T
   constexpr int NCT = DV / 32;      // 32-channel tiles of O^T
   constexpr int KB = DQK / 32;      // channel blocks per K row
@@ -97,9 +101,17 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_kernel(
       const int j = w + kFwdWaves * i;
       if (j < C::NK) dma16(src + koff[i], lds + buf * C::K + j * 1024);
     }
-    if (w < C::NKS)
-      dma16(reinterpret_cast<const uint8_t*>(Kcs + (int64_t)cc * kChunk * KB) + w * 1024 + 16 * lane,
-            lds + C::OFF_KS + buf * C::KS + w * 1024);
+    if constexpr (C::NKS + C::NVS <= kFwdWaves) {  // one scale load per wave
+      if (w < C::NKS)
+        dma16(reinterpret_cast<const uint8_t*>(Kcs + (int64_t)cc * kChunk * KB) + w * 1024 + 16 * lane,
+              lds + C::OFF_KS + buf * C::KS + w * 1024);
+    } else {                                     // scale load j of the chunk on wave j % NW
+#pragma unroll
+      for (int j = 0; j < C::NKS; ++j)
+        if (j % kFwdWaves == w)
+          dma16(reinterpret_cast<const uint8_t*>(Kcs + (int64_t)cc * kChunk * KB) + j * 1024 + 16 * lane,
+                lds + C::OFF_KS + buf * C::KS + j * 1024);
+    }
   };
   auto issue_v = [&](int cc, int buf) {       // V^<s> chunk cc (codes + scales) -> V buffer buf
 #pragma unroll
@@ -107,10 +119,19 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_kernel(
       const int j = w + kFwdWaves * i;
       if (j < C::NV) dma16(Vs + (int64_t)8 * j * Lp + cc * kChunk + voff[i], lds + C::OFF_V + buf * C::V + j * 1024);
     }
-    if (w >= C::NKS && w < C::NKS + C::NVS) {
-      const int j = w - C::NKS;               // channels 64j .. 64j+63, 16 B (4 key blocks) each
-      dma16(Vss + (int64_t)(64 * j + lane) * (Lp / kBlock) + cc * (kChunk / kBlock),
-            lds + C::OFF_VS + buf * C::VS + j * 1024);
+    // V scales: load j covers channels 64j .. 64j+63, 16 B (4 key blocks) each
+    if constexpr (C::NKS + C::NVS <= kFwdWaves) {
+      if (w >= C::NKS && w < C::NKS + C::NVS) {
+        const int j = w - C::NKS;
+        dma16(Vss + (int64_t)(64 * j + lane) * (Lp / kBlock) + cc * (kChunk / kBlock),
+              lds + C::OFF_VS + buf * C::VS + j * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < C::NVS; ++j)
+        if ((C::NKS + j) % kFwdWaves == w)
+          dma16(Vss + (int64_t)(64 * j + lane) * (Lp / kBlock) + cc * (kChunk / kBlock),
+                lds + C::OFF_VS + buf * C::VS + j * 1024);
     }
   };
 
@@ -266,12 +287,13 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_kernel(
 
 template <int DQK, int DV>
 static void launch_fwd_t(const AttnDims& d, Operand q, Operand k, Operand v, float* o, float* lse, hipStream_t s) {
-  dim3 grid((unsigned)((d.Lp + kFwdQ - 1) / kFwdQ) * d.Hq * d.B);
+  constexpr int NW = fwd_waves<DQK, DV>();
+  dim3 grid((unsigned)((d.Lp + 32 * NW - 1) / (32 * NW)) * d.Hq * d.B);
   if (d.causal)
-    hipLaunchKernelGGL((fwd_kernel<DQK, DV, true>), grid, dim3(64 * kFwdWaves), 0, s, q.codes, q.scales, k.codes,
+    hipLaunchKernelGGL((fwd_kernel<DQK, DV, true>), grid, dim3(64 * NW), 0, s, q.codes, q.scales, k.codes,
                        k.scales, v.codes, v.scales, o, lse, d.Hq, d.Hkv, d.L, d.Lp, d.sigma);
   else
-    hipLaunchKernelGGL((fwd_kernel<DQK, DV, false>), grid, dim3(64 * kFwdWaves), 0, s, q.codes, q.scales, k.codes,
+    hipLaunchKernelGGL((fwd_kernel<DQK, DV, false>), grid, dim3(64 * NW), 0, s, q.codes, q.scales, k.codes,
                        k.scales, v.codes, v.scales, o, lse, d.Hq, d.Hkv, d.L, d.Lp, d.sigma);
 }
 
@@ -282,6 +304,7 @@ hipError_t launch_fwd(const AttnDims& d, Operand q, Operand k, Operand v, float*
   else if (d.dqk == 64 && d.dv == 128) launch_fwd_t<64, 128>(d, q, k, v, o, lse, s);
   else if (d.dqk == 128 && d.dv == 64) launch_fwd_t<128, 64>(d, q, k, v, o, lse, s);
   else if (d.dqk == 192 && d.dv == 64) launch_fwd_t<192, 64>(d, q, k, v, o, lse, s);
+  else if (d.dqk == 256 && d.dv == 256) launch_fwd_t<256, 256>(d, q, k, v, o, lse, s);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

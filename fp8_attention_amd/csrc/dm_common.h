@@ -168,8 +168,12 @@ __device__ __forceinline__ int tile_slot(int row, int c) {
     return c ^ ((row >> 1) & 7);
   } else if constexpr (RB == 64) {
     return c ^ ((row >> 2) & 3);
+  } else if constexpr (RB == 256) {
+    // a row spans all 64 banks; XOR with a 4-bit function of the row that takes 16
+    // distinct values on any 16 rows read together, in natural or pair_row order
+    return c ^ ((row & 15) ^ (((row >> 4) & 1) << 3));
   } else {
-    static_assert(RB == 192, "tile rows of 64, 128 or 192 bytes");
+    static_assert(RB == 192, "tile rows of 64, 128, 192 or 256 bytes");
     const int f = ((row >> 2) & 1) | (((row ^ (row >> 3)) & 1) << 1);
     return c < 8 ? (c ^ f) : 8 + ((c - 8) ^ f);
   }
@@ -197,6 +201,11 @@ __device__ __forceinline__ QueryItem query_item(int bid, int nqt, int Hq, int Hk
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
+// One 16-byte-per-lane direct load to the LDS byte address lds_addr (wave-uniform).
+__device__ __forceinline__ void dma16_at(const void* g, uint32_t lds_addr) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+}
 // Issued from inline assembly rather than __builtin_amdgcn_global_load_lds: with the
 // builtin in a kernel the compiler turns every LDS wait into lgkmcnt(0), so reads
 // prefetched for the next tile are waited for together with the current ones.  The
@@ -204,8 +213,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 // explicitly (wait_vmem) before the barrier that publishes a buffer.  The nop is
 // the wait state required between the M0 write and the load that uses it.
 __device__ __forceinline__ void dma16(const void* g, uint8_t* lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((lds_void*)lds_base));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+  dma16_at(g, (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)lds_base));
 }
 // wait for this wave's outstanding global loads (including direct-to-LDS ones)
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

@@ -37,6 +37,9 @@ hipError_t launch_dkdv(const AttnDims& d, Operand qc, Operand qs, Operand kc, Op
 // d_qk = d_v = 128 form of launch_dkdv (attn_dkdv128.hip)
 hipError_t launch_dkdv_d128(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand vc, Operand doc,
                             Operand dos, const float* lse, const float* delta, float* dk, float* dv, hipStream_t s);
+// d_qk = d_v = 256 form of launch_dkdv (attn_dkdv_wide.hip)
+hipError_t launch_dkdv_256_256(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand vc, Operand doc,
+                               Operand dos, const float* lse, const float* delta, float* dk, float* dv, hipStream_t s);
 
 // ps, pa, pc: the row-sum probes (pre-cast sum of dS, sum of |P dP^|, sum of the
 // decoded dS^<k>); ps and pa both null or both set, pc only with them

@@ -58,7 +58,8 @@ class Workload:
 # The five synthetic workloads: a tiny single head, a GQA layer, the long-context
 # GQA layer with near-saturated rows (channel-7 gains 2.0 on Q and 5.4 on K, the
 # key gain the project page reports for stale delta), the 64K context-extension
-# shape, and an MLA-shaped layer with d_qk = 192, d_v = 128.
+# shape, and an MLA-shaped layer with d_qk = 192, d_v = 128; plus the GQA layer at
+# head dimension 256, the head geometry of the project page's larger models.
 WORKLOADS = {
     "tiny": Workload("tiny", 1, 1, 1, 128, 64, 64, False, "iid", seed=1000),
     "gqa_4k": Workload("gqa_4k", 2, 16, 4, 4096, 128, 128, True, "rmsnorm", seed=1001),
@@ -66,6 +67,7 @@ WORKLOADS = {
                        q_gain7=2.0, k_gain7=5.4, seed=1002),
     "gqa_64k": Workload("gqa_64k", 1, 16, 4, 65536, 128, 128, True, "rmsnorm", seed=1003),
     "mla_4k": Workload("mla_4k", 2, 16, 16, 4096, 192, 128, True, "scaled", seed=1004),
+    "gqa_d256_4k": Workload("gqa_d256_4k", 2, 16, 4, 4096, 256, 256, True, "rmsnorm", seed=1005),
 }
 
 

@@ -39,7 +39,10 @@
  *   or beyond L hold zero codes (dm_quantize_blockfp8 writes them).
  * - Formats per operand: Q, K, V and the probabilities in E4M3; dO and dS in
  *   E5M2.
- * - Supported head dims: d_qk in {64, 128, 192}, d_v in {64, 128}.
+ * - Supported head dims: d_qk in {64, 128, 192} with d_v in {64, 128}, and
+ *   d_qk = d_v = 256 (the head geometry of the larger models of the
+ *   Delta-Matching page, section 04 "What changes as the model gets larger?").
+ *   Other pairs return DM_ERR_SHAPE.
  *   Hq must be a multiple of Hkv (GQA: query head h reads KV head h/(Hq/Hkv)).
  *   softmax_scale must be positive and finite.  B, Hq, Hkv >= 1 and L >= 0;
  *   L == 0 is a no-op.

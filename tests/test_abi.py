@@ -63,6 +63,8 @@ BAD_SHAPES = [
     AttnShape(1, 3, 2, 128, 128, 128, True),       # Hq % Hkv != 0
     AttnShape(1, 2, 2, 128, 96, 128, True),        # unsupported d_qk
     AttnShape(1, 2, 2, 128, 128, 192, True),       # unsupported d_v
+    AttnShape(1, 2, 2, 128, 256, 128, True),       # d_qk = 256 only with d_v = 256
+    AttnShape(1, 2, 2, 128, 128, 256, True),       # d_v = 256 only with d_qk = 256
     AttnShape(0, 2, 2, 128, 128, 128, True),       # empty batch
     AttnShape(1, 2, 2, -5, 128, 128, True),        # negative length
     AttnShape(1, 2, 2, 128, 128, 128, True, -1.0),  # non-positive scale

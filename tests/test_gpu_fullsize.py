@@ -38,6 +38,7 @@ CASES = {
     "gqa_8k": (256, 4),
     "gqa_64k": (64, 1),
     "mla_4k": (256, 4),
+    "gqa_d256_4k": (256, 4),
 }
 
 
@@ -126,16 +127,16 @@ def test_fullsize_chain_sampled(name):
         assert np.array_equal(gs, scales), n + " scales"
 
     gsl = (slice(b, b + 1), hs)
-    U.compare("O", o[gsl], f["o"], allow=f["r_o"] + f["b_o"], norm_rel=U.NORM_TOL)
+    U.compare("O", o[gsl], f["o"], allow=f["r_o"] + f["b_o"], norm_rel=U.NORM_TOL, flip=f["r_o"])
     U.compare("LSE", lse[gsl], f["lse"], allow=f["b_lse"], rel=0.0)
     U.compare("delta", delta[gsl], d, allow=derr, rel=0.0)
-    _log("   ", U.compare("dq", dq[gsl], r["dq"], allow=r["r_dq"] + r["b_dq"], norm_rel=U.NORM_TOL))
+    _log("   ", U.compare("dq", dq[gsl], r["dq"], allow=r["r_dq"] + r["b_dq"], norm_rel=U.NORM_TOL, flip=r["r_dq"]))
     keys = np.zeros((1, 1, L, 1), dtype=bool)
     keys[:, :, L - tail:] = True
     ksl = (slice(b, b + 1), slice(g, g + 1))
     for n in ("dk", "dv"):
         t = dk if n == "dk" else dv
-        _log("   ", U.compare(n, t[ksl], r[n], allow=r["r_" + n] + r["b_" + n], norm_rel=U.NORM_TOL,
+        _log("   ", U.compare(n, t[ksl], r[n], allow=r["r_" + n] + r["b_" + n], norm_rel=U.NORM_TOL, flip=r["r_" + n],
                               mask=np.broadcast_to(keys, r[n].shape)))
 
 

@@ -50,6 +50,12 @@ SMALL = {
     # non-causal, mixed head dims, ragged
     "mixed_nc": W.small("mixed_nc", batch=1, heads_q=2, heads_kv=1, seqlen=257, d_qk=64, d_v=128, causal=False,
                         kind="iid", seed=14),
+    # head dimension 256: GQA, causal, ragged (several 64-key dQ chunks, two 128-query tiles)
+    "d256": W.small("d256", batch=1, heads_q=4, heads_kv=2, seqlen=200, d_qk=256, d_v=256, causal=True,
+                    kind="rmsnorm", seed=15),
+    # head dimension 256, non-causal, iid, one key past a 128 boundary
+    "d256_nc": W.small("d256_nc", batch=1, heads_q=2, heads_kv=1, seqlen=129, d_qk=256, d_v=256, causal=False,
+                       kind="iid", seed=16),
 }
 
 
@@ -144,7 +150,7 @@ def test_fwd_parity(name):
     o, lse = api.attn_fwd(shape, ops["q_c"], ops["k_c"], ops["v_s"])
     torch.cuda.synchronize()
     f = ref["fwd"]
-    s = U.compare("O", o, f["o"], allow=f["r_o"] + f["b_o"], norm_rel=U.NORM_TOL)
+    s = U.compare("O", o, f["o"], allow=f["r_o"] + f["b_o"], norm_rel=U.NORM_TOL, flip=f["r_o"])
     U.compare("LSE", lse, f["lse"], allow=f["b_lse"], rel=0.0)
     _log(f"   {s} flagged casts {f['n_flag']} blocks {f['n_block_flag']}")
 
@@ -178,7 +184,7 @@ def test_bwd_parity(name, mode):
     torch.cuda.synchronize()
     b = r["bwd"]
     for n in ("dq", "dk", "dv"):
-        s = U.compare(n, g[n], b[n], allow=b["r_" + n] + b["b_" + n], norm_rel=U.NORM_TOL)
+        s = U.compare(n, g[n], b[n], allow=b["r_" + n] + b["b_" + n], norm_rel=U.NORM_TOL, flip=b["r_" + n])
         _log(f"   {s}")
     # the probe's pre-cast row sums follow the oracle's within the kernel's error bound
     U.compare("rowsum", g["rowsum"], b["rowsum"], allow=b["b_rowsum"] + 1e-30, rel=0.0)
@@ -195,12 +201,12 @@ def test_chain_matched_rowsums_and_parity(name):
     g = api.fwd_delta_bwd(shape, ops, "matched", probe=True)
     torch.cuda.synchronize()
     f, r = ref["fwd"], ref["matched"]
-    U.compare("O", g["o"], f["o"], allow=f["r_o"] + f["b_o"], norm_rel=U.NORM_TOL)
+    U.compare("O", g["o"], f["o"], allow=f["r_o"] + f["b_o"], norm_rel=U.NORM_TOL, flip=f["r_o"])
     derr = A.delta_bound(ref["ops"], shp, "matched", lse=f["lse"], lse_err=f["b_lse"])
     U.compare("delta", g["delta"], r["delta"], allow=derr, rel=0.0)
     b = A.backward(ref["ops"], shp, f["lse"], r["delta"], radius=True, delta_err=derr, lse_err=f["b_lse"])
     for n in ("dq", "dk", "dv"):
-        _log("   ", U.compare(n, g[n], b[n], allow=b["r_" + n] + b["b_" + n], norm_rel=U.NORM_TOL))
+        _log("   ", U.compare(n, g[n], b[n], allow=b["r_" + n] + b["b_" + n], norm_rel=U.NORM_TOL, flip=b["r_" + n]))
     rs, ra = U.to64(g["rowsum"]), U.to64(g["rowabs"])
     assert np.all(np.abs(rs) <= U.ROWSUM_TOL * ra), float(np.max(np.abs(rs) / np.maximum(ra, 1e-300)))
     # the row sums after the E5M2 cast along keys (the third probe)
@@ -213,7 +219,7 @@ def test_chain_matched_rowsums_and_parity(name):
 
 
 @pytest.mark.parametrize("mode", ["stale", "do_matched"])
-@pytest.mark.parametrize("name", ["gqa_ragged", "mla"])
+@pytest.mark.parametrize("name", ["gqa_ragged", "mla", "d256"])
 def test_chain_saved_output_modes(name, mode):
     """Chain with delta from the kernel's own O: the oracle bound carries O's deviation into delta."""
     w, inputs, shape, shp, ref = _case(name)
@@ -265,7 +271,7 @@ def test_run_to_run_determinism():
         assert torch.equal(a[n], b[n]), n
 
 
-@pytest.mark.parametrize("name", ["gqa_ragged", "mla"])
+@pytest.mark.parametrize("name", ["gqa_ragged", "mla", "d256"])
 def test_split_backward_matches_fused(name):
     """dm_attn_bwd_dkdv + dm_attn_bwd_dq (here on two streams) give dm_attn_bwd's bits."""
     w = SMALL[name]
@@ -304,12 +310,12 @@ def test_short_and_ragged_lengths(L):
     g = api.fwd_delta_bwd(shape, ops, "matched", probe=True)
     torch.cuda.synchronize()
     f = ref["fwd"]
-    U.compare("O", g["o"], f["o"], allow=f["r_o"] + f["b_o"], norm_rel=U.NORM_TOL)
+    U.compare("O", g["o"], f["o"], allow=f["r_o"] + f["b_o"], norm_rel=U.NORM_TOL, flip=f["r_o"])
     derr = A.delta_bound(ref["ops"], shp, "matched", lse=f["lse"], lse_err=f["b_lse"])
     b = A.backward(ref["ops"], shp, f["lse"], ref["matched"]["delta"], radius=True, delta_err=derr,
                    lse_err=f["b_lse"])
     for n in ("dq", "dk", "dv"):
-        U.compare(n, g[n], b[n], allow=b["r_" + n] + b["b_" + n], norm_rel=U.NORM_TOL)
+        U.compare(n, g[n], b[n], allow=b["r_" + n] + b["b_" + n], norm_rel=U.NORM_TOL, flip=b["r_" + n])
     # causal row 0 sees only key 0: O_0 equals the decoded V row exactly
     v0 = ref["ops"]["v_s"][0, 0, 0]
     assert np.array_equal(U.to64(g["o"])[0, 0, 0], v0)
