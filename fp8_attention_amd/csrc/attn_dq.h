@@ -1,7 +1,7 @@
 // dQ of block-scaled FP8 attention (query-stationary), with the row-sum probes.
 //
 // Workgroup = 8 waves = 256 queries (32 per wave; 4 waves when the probes are on
-// or d_qk = d_v = 256);
+// or d_qk + d_v > 256);
 // a 1-D grid over (query tile, Hq, B) with the query tile slowest, so the longest
 // causal tiles start first.
 // The wave's Q^<c> and dO^<c> rows sit in registers as the B operands of
@@ -24,9 +24,10 @@
 namespace dm {
 
 // waves per workgroup (32 queries each): 8 (two per SIMD); the probe variant, with
-// its extra row sums live, and d_qk = d_v = 256, with 256-channel dQ accumulators,
-// run one wave per SIMD with the full register file
-template <bool PROBE, int DQK, int DV> constexpr int dq_waves() { return (PROBE || DQK + DV > 384) ? 4 : 8; }
+// its extra row sums live, and head dims beyond d_qk + d_v = 256 (192/128: spills at
+// two waves per SIMD and runs 25% faster at one; 256/256) run one wave per SIMD with
+// the full register file (accumulators in AGPRs)
+template <bool PROBE, int DQK, int DV> constexpr int dq_waves() { return (PROBE || DQK + DV > 256) ? 4 : 8; }
 // keys per LDS chunk: 128, or 64 when d_qk = d_v = 256 (two chunks of K^<c>, V^<c>
 // and K^<s> at 128 keys would not fit in LDS)
 template <int DQK, int DV> constexpr int dq_chunk() { return DQK + DV > 384 ? 64 : 128; }
