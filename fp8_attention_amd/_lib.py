@@ -47,8 +47,7 @@ def load() -> ctypes.CDLL:
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
-                           "or `python fp8_attention_amd/build.py`")
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python fp8_attention_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.dm_padded_len.argtypes = [i64]
