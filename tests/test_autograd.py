@@ -72,6 +72,7 @@ CHAIN_CASES = [
     (2, 4, 2, 129, 64, 64, False, "stale", torch.bfloat16),
     (1, 2, 2, 257, 192, 128, True, "do_matched", torch.bfloat16),
     (1, 4, 1, 320, 128, 128, True, "matched", torch.float32),
+    (1, 2, 1, 129, 256, 256, True, "matched", torch.bfloat16),
 ]
 
 
