@@ -204,14 +204,15 @@ typedef __attribute__((address_space(3))) void lds_void;
 // One 16-byte-per-lane direct load to the LDS byte address lds_addr (wave-uniform).
 __device__ __forceinline__ void dma16_at(const void* g, uint32_t lds_addr) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0) : "memory");
 }
 // Issued from inline assembly rather than __builtin_amdgcn_global_load_lds: with the
 // builtin in a kernel the compiler turns every LDS wait into lgkmcnt(0), so reads
 // prefetched for the next tile are waited for together with the current ones.  The
 // hardware tracks these loads with VM_CNT only; every kernel waits for them
-// explicitly (wait_vmem) before the barrier that publishes a buffer.  The nop is
-// the wait state required between the M0 write and the load that uses it.
+// explicitly (wait_vmem) before the barrier that publishes a buffer.  M0 (the LDS
+// address) is an operand bound to that register, so the compiler writes it; the
+// nop is the wait state required between the M0 write and the load that uses it.
 __device__ __forceinline__ void dma16(const void* g, uint8_t* lds_base) {
   dma16_at(g, (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)lds_base));
 }
