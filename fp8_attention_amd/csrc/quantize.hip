@@ -70,15 +70,19 @@ __global__ __launch_bounds__(256) void quantize_cols_kernel(const T* __restrict_
 }
 
 // Blocks along rows, output transposed.  A workgroup takes a tile of 128 rows x
-// 64 columns, stages it in LDS as float (column-major, padded), then each of the
-// 256 threads quantizes one (column, 32-row block) and writes 32 contiguous codes.
-constexpr int kTR = 128, kTC = 64, kTRP = kTR + 4;
+// 64 columns, stages it in LDS as float (column-major), then each of the 256
+// threads quantizes one (column, 32-row block) and writes 32 contiguous codes.
+// Row index bits 3-5 are XORed with bits 3-5 of the column: the eight lanes that
+// stage one row (columns 8 apart) then write eight different bank groups, and each
+// column's rows stay in contiguous 8-float chunks for the 16-byte reads.
+constexpr int kTR = 128, kTC = 64;
+__device__ __forceinline__ int tile_pos(int col, int row) { return col * kTR + (row ^ (col & 0x38)); }
 
 template <typename T, int F>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const T* __restrict__ x, int64_t rows, int64_t cols,
                                                             int64_t rows_out, uint8_t* __restrict__ codes,
                                                             float* __restrict__ scales) {
-  __shared__ float tile[kTC * kTRP];
+  __shared__ float tile[kTC * kTR];
   const int64_t b = blockIdx.z;
   const int64_t r0 = (int64_t)blockIdx.x * kTR;
   const int64_t c0 = (int64_t)blockIdx.y * kTC;
@@ -98,19 +102,18 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const T* __restrict_
       for (int i = 0; i < 8; ++i) v[i] = 0.f;
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) tile[(cc + i) * kTRP + rr] = v[i];
+    for (int i = 0; i < 8; ++i) tile[tile_pos(cc + i, rr)] = v[i];
   }
   __syncthreads();
   const int cc = t >> 2, blk = t & 3;
   const int64_t c = c0 + cc;
   const int64_t r = r0 + blk * kBlock;
   if (c >= cols || r >= rows_out) return;
-  const float* src = tile + cc * kTRP + blk * kBlock;
   float v[32];
   float am = 0.f;
 #pragma unroll
   for (int i = 0; i < 32; i += 4) {
-    v4f q = *reinterpret_cast<const v4f*>(src + i);
+    v4f q = *reinterpret_cast<const v4f*>(tile + tile_pos(cc, blk * kBlock + i));
     v[i] = q[0]; v[i + 1] = q[1]; v[i + 2] = q[2]; v[i + 3] = q[3];
     am = fmaxf(am, fmaxf(fmaxf(fabsf(q[0]), fabsf(q[1])), fmaxf(fabsf(q[2]), fabsf(q[3]))));
   }
