@@ -218,6 +218,43 @@ def test_chain_matched_rowsums_and_parity(name):
               allow=b["r_rowsum_cast"] + b["b_rowsum_cast"] + 1e-30, rel=0.0)
 
 
+GROUP_SCALE_CASES = {
+    # multi-query attention (one KV head for 8 query heads: the dK/dV head loop at its longest) with a
+    # softmax scale other than 1/sqrt(d); the same at head dim 256; MLA dims, non-causal, small scale
+    "mqa_d128_s0.25": (W.small("mqa128", batch=1, heads_q=8, heads_kv=1, seqlen=192, d_qk=128, d_v=128,
+                                causal=True, kind="rmsnorm", seed=21), 0.25),
+    "mqa_d256": (W.small("mqa256", batch=1, heads_q=4, heads_kv=1, seqlen=160, d_qk=256, d_v=256, causal=True,
+                         kind="rmsnorm", seed=22), None),
+    "mla_nc_s0.05": (W.small("mla_nc", batch=2, heads_q=2, heads_kv=2, seqlen=130, d_qk=192, d_v=128,
+                             causal=False, kind="scaled", seed=23), 0.05),
+}
+
+
+@pytest.mark.parametrize("name", list(GROUP_SCALE_CASES))
+def test_chain_query_groups_and_softmax_scale(name):
+    """The matched chain with a large query group and an explicit softmax scale, against the oracle."""
+    w, scale = GROUP_SCALE_CASES[name]
+    api = _api()
+    shape = api.AttnShape(w.batch, w.heads_q, w.heads_kv, w.seqlen, w.d_qk, w.d_v, w.causal, scale)
+    shp = U.oracle_shape(w, shape.sigma)
+    inputs = W.generate(w)
+    _log(f"[chain groups/scale] {name} sigma={shape.sigma}")
+    ref = U.run_oracle(inputs, shp, modes=("matched",))
+    _, ops = _gpu_ops(inputs)
+    g = api.fwd_delta_bwd(shape, ops, "matched", probe=True)
+    torch.cuda.synchronize()
+    f, r = ref["fwd"], ref["matched"]
+    U.compare("O", g["o"], f["o"], allow=f["r_o"] + f["b_o"], norm_rel=U.NORM_TOL, flip=f["r_o"])
+    U.compare("LSE", g["lse"], f["lse"], allow=f["b_lse"], rel=0.0)
+    derr = A.delta_bound(ref["ops"], shp, "matched", lse=f["lse"], lse_err=f["b_lse"])
+    U.compare("delta", g["delta"], r["delta"], allow=derr, rel=0.0)
+    b = A.backward(ref["ops"], shp, f["lse"], r["delta"], radius=True, delta_err=derr, lse_err=f["b_lse"])
+    for n in ("dq", "dk", "dv"):
+        _log("   ", U.compare(n, g[n], b[n], allow=b["r_" + n] + b["b_" + n], norm_rel=U.NORM_TOL, flip=b["r_" + n]))
+    rs, ra = U.to64(g["rowsum"]), U.to64(g["rowabs"])
+    assert np.all(np.abs(rs) <= U.ROWSUM_TOL * ra), float(np.max(np.abs(rs) / np.maximum(ra, 1e-300)))
+
+
 @pytest.mark.parametrize("mode", ["stale", "do_matched"])
 @pytest.mark.parametrize("name", ["gqa_ragged", "mla", "d256"])
 def test_chain_saved_output_modes(name, mode):
