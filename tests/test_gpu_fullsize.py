@@ -171,3 +171,36 @@ def test_postcast_rowsum_residual_stale_vs_matched(name):
          f"(matched {np.mean(res['matched'][0]):.2e}), after the cast {post:.2f}x "
          f"(stale {np.mean(res['stale'][1]):.3e}, matched {np.mean(res['matched'][1]):.3e})")
     assert post > 1.0
+
+
+@pytest.mark.parametrize("name", ["gqa_8k", "gqa_64k"])
+def test_saved_output_deltas_every_row(name):
+    """The stale and dO-matched corrections at full size, every row, as properties of the kernel's
+    inputs: delta_i = sum_k dO_ik O_ik (bf16 dO) and sum_k dO^_ik O_ik (dO^ decoded from its E5M2 codes
+    and block scales, codes the quantize tests check bit for bit), evaluated in float64 from the same O
+    the kernel is given.  Bound: FP32 accumulation, 2^-20 of sum_k |dO_ik O_ik| (d = 128 terms)."""
+    from fp8_attention_amd import api
+    w = W.WORKLOADS[name]
+    inputs = W.generate(w)
+    do = inputs["do"].cuda()
+    B, Hq, L, D = w.batch, w.heads_q, w.seqlen, w.d_v
+    shape = api.AttnShape(B, Hq, w.heads_kv, L, w.d_qk, D, w.causal)
+    # any FP32 O of the right shape exercises the pass; a seeded one keeps the forward out of it
+    o = torch.randn((B, Hq, L, D), generator=torch.Generator().manual_seed(7), dtype=torch.float32).cuda()
+    do_c = api.quantize(do, "cols", "e5m2", api.padded_len(L))
+    for mode in ("stale", "do_matched"):
+        if mode == "stale":
+            got = api.attn_delta(shape, mode, o=o, do=do)
+            x = do.double()
+        else:
+            got = api.attn_delta(shape, mode, o=o, do_c=do_c)
+            codes = do_c.codes[..., :L, :].view(torch.float8_e5m2).double()
+            x = codes * do_c.scales[..., :L, :].double().repeat_interleave(32, dim=-1)
+        torch.cuda.synchronize()
+        prod = x * o.double()
+        ref, mag = prod.sum(-1), prod.abs().sum(-1)
+        err = (got.double() - ref).abs()
+        worst = float((err / mag.clamp_min(1e-300)).max())
+        _log(f"   {name} {mode}: max |err| / sum|dO O| = {worst:.2e} over {ref.numel()} rows")
+        assert bool((err <= 2.0 ** -20 * mag + 1e-30).all()), worst
+        del prod, ref, mag, err, x
