@@ -8,7 +8,7 @@ the row correction delta in the chosen mode and runs the FP8 backward
 (Delta-Matching page, section 01 "Write down softmax backward" and "What
 changes in FP8?"; section 03 for the matched correction).
 
-Modes of delta ("Why can we reuse the output?" and section 03 of that page):
+Modes of delta (section 01 "Why can we reuse the forward output?" and section 03 of that page):
   * ``"matched"`` (default) -- sum_j P_ij dP^_ij from the backward's own FP8
     operands; the rows of dS then sum to zero up to FP32 rounding;
   * ``"do_matched"`` -- sum_k dO^_ik O_ik with the quantized dO;
