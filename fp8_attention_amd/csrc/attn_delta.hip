@@ -96,6 +96,14 @@ hipError_t launch_delta_rows(const AttnDims& d, int mode, const float* o, const 
 // waves per workgroup (32 queries each): two per SIMD; one per SIMD when
 // d_qk = d_v = 256, whose Q, dO rows and score tiles fill more than half the file
 template <int DQK, int DV> constexpr int delta_waves() { return DQK + DV > 384 ? 4 : 8; }
+// Up to d_qk + d_v = 256 a lean form keeps one score tile live at a time and fits in
+// 128 VGPRs, so two workgroups share a CU (four waves per SIMD, 72 KB of LDS each) and
+// the waves interleave their MFMA and softmax work: 8% faster than prefetching the next
+// chunk's tiles at two waves per SIMD on large grids (8K, 64K), slower on small ones
+// (4K: two unequal causal tiles per CU), so the launcher picks it for grids of at least
+// four workgroups per CU.  Wider heads would spill at 128 and only have the prefetching
+// form, which overlaps within the wave instead.
+template <int DQK, int DV> constexpr bool delta_lean_ok() { return DQK + DV <= 256; }
 
 template <int DQK, int DV>
 struct DeltaLds {
@@ -114,11 +122,13 @@ struct DeltaLds {
 // Workgroup = 8 waves = 256 queries (4 waves = 128 when d = 256); 1-D grid over (query tile, Hq, B), query
 // tile slowest and the longest causal tiles first.  Per 128-key chunk and 32-key tile:
 // S^T = K Q^T and dP^T = V dO^T (lane pair = query, 16 keys per lane), then
-// delta += sum P * dP^ with P = exp2(S sigma log2e - LSE log2e).  The tiles of
-// chunk c+1 are computed as soon as tile t of chunk c has been consumed; K^<c> /
-// V^<c> chunks are double-buffered in LDS via direct global->LDS loads.
-template <int DQK, int DV, bool CAUSAL>
-__global__ __launch_bounds__((64 * delta_waves<DQK, DV>())) void delta_matched_kernel(
+// delta += sum P * dP^ with P = exp2(S sigma log2e - LSE log2e).  K^<c> / V^<c>
+// chunks are double-buffered in LDS via direct global->LDS loads.  Two loop forms
+// (LEAN): one tile live at four waves per SIMD, or the tiles of
+// chunk c+1 computed as soon as tile t of chunk c has been consumed.  Both accumulate
+// in the same order, so they give the same bits.
+template <int DQK, int DV, bool CAUSAL, bool LEAN>
+__global__ __launch_bounds__((64 * delta_waves<DQK, DV>()), (LEAN ? 4 : 1)) void delta_matched_kernel(
     const uint8_t* __restrict__ qc, const float* __restrict__ qcs, const uint8_t* __restrict__ kc,
     const float* __restrict__ kcs, const uint8_t* __restrict__ vc, const float* __restrict__ vcs,
     const uint8_t* __restrict__ doc, const float* __restrict__ docs, const float* __restrict__ lse,
@@ -246,6 +256,36 @@ __global__ __launch_bounds__((64 * delta_waves<DQK, DV>())) void delta_matched_k
 
   issue(0, 0);
   if (nchunks > 1) issue(1, 1);
+  if constexpr (LEAN) {
+    // one tile at a time; chunk c+1 is loaded while chunk c is consumed
+    for (int c = 0; c < nchunks; ++c) {
+      const int k0 = c * kChunk;
+      wait_vmem();
+      __syncthreads();                           // chunk c landed; buffer (c+1)%2 free
+      if (c >= 1 && c + 1 < nchunks) issue(c + 1, (c + 1) & 1);
+      if (!live || c > wlast) continue;
+      const bool mask = (k0 + kChunk > L) || (CAUSAL && k0 + kChunk - 1 > qw);
+      const int lim = (CAUSAL ? min(qi, L - 1) : L - 1) - (k0 + 16 * h);   // key k0+32t+16h+v visible iff 32t+v <= lim
+      float cacc = 0.f, pc = 0.f;
+#pragma unroll 1
+      for (int t = 0; t < 4; ++t) {
+        v16f s, dp;
+        tiles(c & 1, t, s, dp);
+        if (mask) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) s[v] = (32 * t + v > lim) ? -INFINITY : s[v];
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[v], c2, -l2));
+          cacc = fmaf(p, dp[v], cacc);
+          pc += p;
+        }
+      }
+      acc += (double)cacc;
+      psum += (double)pc;
+    }
+  } else {
   wait_vmem();
   __syncthreads();
   v16f s[4], dp[4];
@@ -285,6 +325,7 @@ __global__ __launch_bounds__((64 * delta_waves<DQK, DV>())) void delta_matched_k
     acc += (double)cacc;
     psum += (double)pc;
   }
+  }
   if (!live) return;
   acc = pair_sum_d(acc);
   psum = pair_sum_d(psum);
@@ -296,15 +337,25 @@ template <int DQK, int DV>
 static void launch_dm_t(const AttnDims& d, Operand doc, Operand q, Operand k, Operand v, const float* lse,
                         float* delta, hipStream_t s) {
   constexpr int NW = delta_waves<DQK, DV>();
-  dim3 grid((unsigned)((d.Lp + 32 * NW - 1) / (32 * NW)) * d.Hq * d.B);
-  if (d.causal)
-    hipLaunchKernelGGL((delta_matched_kernel<DQK, DV, true>), grid, dim3(64 * NW), 0, s, q.codes, q.scales,
-                       k.codes, k.scales, v.codes, v.scales, doc.codes, doc.scales, lse, delta, d.Hq, d.Hkv, d.L,
-                       d.Lp, d.sigma);
-  else
-    hipLaunchKernelGGL((delta_matched_kernel<DQK, DV, false>), grid, dim3(64 * NW), 0, s, q.codes, q.scales,
-                       k.codes, k.scales, v.codes, v.scales, doc.codes, doc.scales, lse, delta, d.Hq, d.Hkv, d.L,
-                       d.Lp, d.sigma);
+  const unsigned nblk = (unsigned)((d.Lp + 32 * NW - 1) / (32 * NW)) * d.Hq * d.B;
+  int ncu = 256;
+  {
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  }
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(nblk), dim3(64 * NW), 0, s, q.codes, q.scales, k.codes, k.scales, v.codes,
+                       v.scales, doc.codes, doc.scales, lse, delta, d.Hq, d.Hkv, d.L, d.Lp, d.sigma);
+  };
+  if constexpr (delta_lean_ok<DQK, DV>()) {
+    if (nblk >= 4u * (unsigned)ncu) {
+      if (d.causal) go(delta_matched_kernel<DQK, DV, true, true>);
+      else go(delta_matched_kernel<DQK, DV, false, true>);
+      return;
+    }
+  }
+  if (d.causal) go(delta_matched_kernel<DQK, DV, true, false>);
+  else go(delta_matched_kernel<DQK, DV, false, false>);
 }
 
 hipError_t launch_delta_matched(const AttnDims& d, Operand doc, Operand q, Operand k, Operand v, const float* lse,
