@@ -68,13 +68,45 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
 
 
-def _need(t: torch.Tensor, name: str, dtype=None):
+def _need(t: torch.Tensor, name: str, dtype=None, device=None):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other arguments on {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _op_shapes(shape: AttnShape, name: str):
+    """Expected (codes, scales) shapes of operand ``name`` (q_c, q_s, k_c, k_s, v_c, v_s, do_c, do_s)."""
+    B, Lp = shape.batch, padded_len(shape.seqlen)
+    H = shape.heads_q if name[0] in "qd" else shape.heads_kv     # Q, dO per query head; K, V per KV head
+    d = shape.d_qk if name[0] in "qk" else shape.d_v
+    if name.endswith("_c"):
+        return (B, H, Lp, d), (B, H, Lp, d // 32)
+    return (B, H, d, Lp), (B, H, d, Lp // 32)
+
+
+def _need_op(shape: AttnShape, op: Fp8Operand, name: str, device) -> None:
+    """A quantized operand: GPU, contiguous, uint8 codes and float32 scales of the layout the kernels read."""
+    _need(op.codes, name + ".codes", torch.uint8, device)
+    _need(op.scales, name + ".scales", torch.float32, device)
+    if shape.seqlen > 0:
+        cs, ss = _op_shapes(shape, name)
+        if tuple(op.codes.shape) != cs or tuple(op.scales.shape) != ss:
+            raise ValueError(f"{name}: codes {tuple(op.codes.shape)} / scales {tuple(op.scales.shape)}, "
+                             f"expected {cs} / {ss}")
+
+
+def _need_t(shape: AttnShape, t: Optional[torch.Tensor], name: str, dims, device, dtype=torch.float32) -> None:
+    """A dense input or output ([B, H, L] or [B, H, L, d]) of the given dtype, when given."""
+    if t is None:
+        return
+    _need(t, name, dtype, device)
+    if shape.seqlen > 0 and tuple(t.shape) != tuple(dims):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(dims)}")
 
 
 def quantize(x: torch.Tensor, axis: str = "cols", fmt: str = "e4m3", rows_out: Optional[int] = None) -> Fp8Operand:
@@ -127,6 +159,10 @@ def attn_fwd(shape: AttnShape, q_c: Fp8Operand, k_c: Fp8Operand, v_s: Fp8Operand
     """dm_attn_fwd -> (O [B,Hq,L,d_v] float32, LSE [B,Hq,L] float32)."""
     dev = q_c.codes.device
     B, Hq, L = shape.batch, shape.heads_q, shape.seqlen
+    for n, op in (("q_c", q_c), ("k_c", k_c), ("v_s", v_s)):
+        _need_op(shape, op, n, dev)
+    _need_t(shape, o, "o", (B, Hq, L, shape.d_v), dev)
+    _need_t(shape, lse, "lse", (B, Hq, L), dev)
     if o is None:
         o = torch.empty((B, Hq, L, shape.d_v), dtype=torch.float32, device=dev)
     if lse is None:
@@ -146,10 +182,17 @@ def attn_delta(shape: AttnShape, mode: str, *, o: Optional[torch.Tensor] = None,
     if mode not in MODES:
         raise ValueError(f"unknown delta mode {mode!r}")
     ref = next(t for t in (o, lse, do, None if do_c is None else do_c.codes) if t is not None)
+    dev = ref.device
+    B, Hq, L = shape.batch, shape.heads_q, shape.seqlen
+    _need_t(shape, o, "o", (B, Hq, L, shape.d_v), dev)
+    _need_t(shape, do, "do", (B, Hq, L, shape.d_v), dev, torch.bfloat16)
+    _need_t(shape, lse, "lse", (B, Hq, L), dev)
+    _need_t(shape, out, "out", (B, Hq, L), dev)
+    for n, op in (("do_c", do_c), ("q_c", q_c), ("k_c", k_c), ("v_c", v_c)):
+        if op is not None:
+            _need_op(shape, op, n, dev)
     if out is None:
-        out = torch.empty((shape.batch, shape.heads_q, shape.seqlen), dtype=torch.float32, device=ref.device)
-    if do is not None:
-        _need(do, "do", torch.bfloat16)
+        out = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
     cs = shape.c()
     opc = lambda x: _NULL_OPERAND if x is None else x.c()  # noqa: E731
     st = _lib.load().dm_attn_delta(ctypes.byref(cs), MODES[mode], _ptr(o), _ptr(do), opc(do_c), opc(q_c),
@@ -158,10 +201,23 @@ def attn_delta(shape: AttnShape, mode: str, *, o: Optional[torch.Tensor] = None,
     return out
 
 
+def _need_bwd(shape: AttnShape, ops: dict, names, lse, delta, dq=None, dk=None, dv=None):
+    dev = lse.device
+    B, Hq, Hkv, L = shape.batch, shape.heads_q, shape.heads_kv, shape.seqlen
+    for n in names:
+        _need_op(shape, ops[n], n, dev)
+    _need_t(shape, lse, "lse", (B, Hq, L), dev)
+    _need_t(shape, delta, "delta", (B, Hq, L), dev)
+    _need_t(shape, dq, "dq", (B, Hq, L, shape.d_qk), dev)
+    _need_t(shape, dk, "dk", (B, Hkv, L, shape.d_qk), dev)
+    _need_t(shape, dv, "dv", (B, Hkv, L, shape.d_v), dev)
+
+
 def attn_bwd(shape: AttnShape, ops: dict, lse: torch.Tensor, delta: torch.Tensor, probe: bool = False,
              dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
              dv: Optional[torch.Tensor] = None) -> dict:
     """dm_attn_bwd -> {"dq","dk","dv"} float32 (+ "rowsum","rowabs" float64 probes when probe=True)."""
+    _need_bwd(shape, ops, ("q_c", "q_s", "k_c", "k_s", "v_c", "do_c", "do_s"), lse, delta, dq, dk, dv)
     dev = lse.device
     B, Hq, Hkv, L = shape.batch, shape.heads_q, shape.heads_kv, shape.seqlen
     if dq is None:
@@ -188,6 +244,7 @@ def attn_bwd(shape: AttnShape, ops: dict, lse: torch.Tensor, delta: torch.Tensor
 def attn_bwd_dkdv(shape: AttnShape, ops: dict, lse: torch.Tensor, delta: torch.Tensor,
                   dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None) -> dict:
     """dm_attn_bwd_dkdv -> {"dk","dv"} float32 (the key-stationary half of dm_attn_bwd)."""
+    _need_bwd(shape, ops, ("q_c", "q_s", "k_c", "v_c", "do_c", "do_s"), lse, delta, dk=dk, dv=dv)
     dev = lse.device
     B, Hkv, L = shape.batch, shape.heads_kv, shape.seqlen
     if dk is None:
@@ -208,6 +265,7 @@ def attn_bwd_dq(shape: AttnShape, ops: dict, lse: torch.Tensor, delta: torch.Ten
 
     With ``probe_cast`` (dm_attn_bwd_dq_probes) also "rowsum_cast": the row sums of dS
     after its E5M2 cast along keys (implies ``probe``)."""
+    _need_bwd(shape, ops, ("q_c", "k_c", "k_s", "v_c", "do_c"), lse, delta, dq=dq)
     dev = lse.device
     B, Hq, L = shape.batch, shape.heads_q, shape.seqlen
     if dq is None:
