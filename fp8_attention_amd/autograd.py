@@ -19,8 +19,8 @@ multiple of Hkv: grouped-query attention; dK and dV are summed over each
 group), contiguous, bfloat16 or float32, on the GPU.  The output and the
 gradients come back in the inputs' dtype.  dO enters the backward as bfloat16
 (the stale mode is defined on the bf16 dO).  The context keeps the six FP8
-operands (1 byte per element and layout plus the scales), the FP32 output
-(read by the stale and dO-matched modes) and the log-sum-exp.
+operands (1 byte per element and layout plus the scales), the log-sum-exp and,
+for the stale and dO-matched modes, which read it, the FP32 output.
 """
 from __future__ import annotations
 
@@ -73,7 +73,9 @@ class Fp8Attention(torch.autograd.Function):
         names = [n for n, *_ in _QUANT]
         ctx.names = names
         ctx.shape, ctx.mode, ctx.dtypes = shape, delta_mode, (q.dtype, k.dtype, v.dtype)
-        ctx.save_for_backward(o, lse, *[t for n in names for t in ops[n]])
+        # the FP32 output is read back only by the saved-output modes
+        keep_o = o if delta_mode != "matched" else torch.empty(0, device=o.device)
+        ctx.save_for_backward(keep_o, lse, *[t for n in names for t in ops[n]])
         return o if q.dtype == torch.float32 else o.to(q.dtype)
 
     @staticmethod
