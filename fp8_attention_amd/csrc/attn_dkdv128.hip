@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kSTAGE];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int n = lane & 15, g = lane >> 4;              // key column / lane group of the 16x16 tiles
   const int nkt = Lp / kKT;
   const int nhb = Hkv * (int)(gridDim.x / (nkt * Hkv));    // Hkv * B
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
   }
 
   // ---- direct loads: per wave two 1 KB pieces of each 16 KB tile and one piece of the scales
-  int orow[2], ochan[2];                             // per-lane source offsets (loop invariant)
+  uint32_t orow[2], ochan[2];                        // per-lane source offsets (loop invariant)
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int r = 8 * (w + 8 * i) + (lane >> 3);     // LDS row this lane fills
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
   }
   const int sel = w >> 1;                            // 0 Q^<c>, 1 dO^<c>, 2 Q^<s>, 3 dO^<s> scales
   const int srow = 64 * (w & 1) + lane;
-  const int oscale = sel < 2 ? qrow(srow >> 4, srow & 15) * 16 : srow * LB * 4;
+  const uint32_t oscale = sel < 2 ? qrow(srow >> 4, srow & 15) * 16 : srow * LB * 4;
   const uint8_t* const sbase = reinterpret_cast<const uint8_t*>(sel == 0 ? qcs : sel == 1 ? docs : sel == 2 ? qss : doss);
   const int sdst = kQCS + 1024 * w;
   // base pointers of one step's loads (wave-uniform)
@@ -120,31 +120,36 @@ __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
   // one of the step's nine direct loads of this wave (part is a constant after unrolling)
   auto issue_part = [&](int part, const Src& sr, uint8_t* st) {
     if (part == 8) {
-      dma16(sr.sc + oscale, st + sdst);
+      dma16s(sr.sc, oscale, st + sdst);
       return;
     }
     const int i = part >> 2, which = part & 3;
     const int dst = 1024 * (w + 8 * i);
-    if (which == 0) dma16(sr.q + orow[i], st + kQC + dst);
-    else if (which == 1) dma16(sr.d + orow[i], st + kDOC + dst);
-    else if (which == 2) dma16(sr.qs + ochan[i], st + kQS + dst);
-    else dma16(sr.ds + ochan[i], st + kDOS + dst);
+    if (which == 0) dma16s(sr.q, orow[i], st + kQC + dst);
+    else if (which == 1) dma16s(sr.d, orow[i], st + kDOC + dst);
+    else if (which == 2) dma16s(sr.qs, ochan[i], st + kQS + dst);
+    else dma16s(sr.ds, ochan[i], st + kDOS + dst);
   };
   auto issue = [&](const Src& sr, uint8_t* st) {
 #pragma unroll
     for (int part = 0; part < 9; ++part) issue_part(part, sr, st);
   };
   // LSE (in log2 units) and delta of the step's queries through registers (threads
-  // 0-127 and 128-255; the others load an in-range value they do not store)
-  float smallv = 0.f;
+  // 0-127 and 128-255; the others load an in-range value they do not store).  The
+  // load is unconditional and its value is first used when it is stored at the end
+  // of the step, so its latency hides behind the step (a select next to the load
+  // made the compiler put the load in a branch and wait for it at once).
+  float smallx = 0.f;
+  bool smallpad = false;
   auto load_small = [&](int64_t qhead, int q0) {
     const int q = q0 + (tid & (kQT - 1));
-    const bool is_lse = tid < kQT;
-    const float x = (is_lse ? lse : delta)[qhead * L + min(q, L - 1)];
-    smallv = q < L ? (is_lse ? x * kLog2e : x) : (is_lse ? INFINITY : 0.f);   // padded queries: P = 0
+    smallx = (tid < kQT ? lse : delta)[qhead * L + min(q, L - 1)];
+    smallpad = q >= L;
   };
   auto store_small = [&](uint8_t* st) {
-    if (tid < 2 * kQT) reinterpret_cast<float*>(st + kLSE)[tid] = smallv;
+    const bool is_lse = tid < kQT;
+    const float v = smallpad ? (is_lse ? INFINITY : 0.f) : (is_lse ? smallx * kLog2e : smallx);  // padded: P = 0
+    if (tid < 2 * kQT) reinterpret_cast<float*>(st + kLSE)[tid] = v;
   };
 
   v4f accv[kD / 16], acck[kD / 16];                  // dV^T, dK^T channel tiles: reg i <-> channel 16ct+4g+i
@@ -187,6 +192,19 @@ __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
       const float* delp = lsep + kQT;
       const float* qcsp = reinterpret_cast<const float*>(st + kQCS) + 4 * n + g;
       const float* docsp = reinterpret_cast<const float*>(st + kDOCS) + 4 * n + g;
+      // S and dP^ of tile t (and the next step's direct load that goes with it)
+      auto tile_mm = [&](int t, v4f& s, v4f& dp) {
+        issue_part(t + (t == 0 ? 8 : 0), nx, stn);     // next step's loads, spread over the tiles
+        if (t == 0) issue_part(0, nx, stn);
+        const v8i aq = cat(lds_read16(st + kQC + 2048 * t + ra0), lds_read16(st + kQC + 2048 * t + ra1));
+        s = mfma16<E4M3, E4M3>(aq, kb, v4f{}, e8m0(qcsp[64 * t]), ksc);
+        const v8i ad = cat(lds_read16(st + kDOC + 2048 * t + ra0), lds_read16(st + kDOC + 2048 * t + ra1));
+        dp = mfma16<E5M2, E4M3>(ad, vb, v4f{}, e8m0(docsp[64 * t]), vsc);
+      };
+      // software pipeline: the products of tile t+1 are issued before the FP32 work on
+      // tile t, so that work does not wait for the matrix core
+      v4f s_nx, dp_nx;
+      tile_mm(0, s_nx, dp_nx);
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         // tiles 4hf .. 4hf+3: lane (n, g) holds queries 64hf + 16g + 4tt + i
@@ -194,12 +212,8 @@ __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
           const int t = 4 * hf + tt;
-          issue_part(t + (t == 0 ? 8 : 0), nx, stn);   // next step's loads, spread over the tiles
-          if (t == 0) issue_part(0, nx, stn);
-          const v8i aq = cat(lds_read16(st + kQC + 2048 * t + ra0), lds_read16(st + kQC + 2048 * t + ra1));
-          const v4f s = mfma16<E4M3, E4M3>(aq, kb, v4f{}, e8m0(qcsp[64 * t]), ksc);
-          const v8i ad = cat(lds_read16(st + kDOC + 2048 * t + ra0), lds_read16(st + kDOC + 2048 * t + ra1));
-          const v4f dp = mfma16<E5M2, E4M3>(ad, vb, v4f{}, e8m0(docsp[64 * t]), vsc);
+          const v4f s = s_nx, dp = dp_nx;
+          if (t + 1 < 8) tile_mm(t + 1, s_nx, dp_nx);
           const v4f l4 = *reinterpret_cast<const v4f*>(lsep + 64 * hf + 4 * tt);
           const v4f d4 = *reinterpret_cast<const v4f*>(delp + 64 * hf + 4 * tt);
 #pragma unroll

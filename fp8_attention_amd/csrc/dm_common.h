@@ -216,6 +216,14 @@ __device__ __forceinline__ void dma16_at(const void* g, uint32_t lds_addr) {
 __device__ __forceinline__ void dma16(const void* g, uint8_t* lds_base) {
   dma16_at(g, (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)lds_base));
 }
+// The same load in the SADDR form: a wave-uniform 64-bit base (SGPRs) plus a
+// 32-bit unsigned per-lane byte offset, so a loop that keeps its per-lane offsets
+// spends no vector instructions on addresses; with a wave-uniform LDS destination
+// the M0 write is scalar too.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint8_t* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((lds_void*)lds_base));
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(m0) : "memory");
+}
 // wait for this wave's outstanding global loads (including direct-to-LDS ones)
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
