@@ -218,18 +218,35 @@ __global__ __launch_bounds__((64 * dq_waves<PROBE, DQK, DV>())) void dq_kernel(
     v8i dsb[NST];
     int dssc[NST] = {};
     float csum = 0.f, cabs = 0.f, ccast = 0.f;
-#pragma unroll
-    for (int t = 0; t < NTL; ++t) {
-      // dP^T tile t of chunk c
+    // dP^T tile t of chunk c
+    auto dp_tile = [&](int t) -> v16f {
       const float* vsr = reinterpret_cast<const float*>(vp + C::OFF_VS) + (32 * t + kr) * VB;
-      v16f dp = v16f{};
+      v16f dp_ = v16f{};
 #pragma unroll
       for (int ks = 0; ks < VS; ++ks) {
         const uint8_t* p = vp + 32 * t * DV;
         const v8i a = cat(lds_read16(p + vro[ks][0]), lds_read16(p + vro[ks][1]));
-        dp = mfma<E4M3, E5M2>(a, db[ks], dp, e8m0(vsr[2 * ks + h]), dsc[ks]);
+        dp_ = mfma<E4M3, E5M2>(a, db[ks], dp_, e8m0(vsr[2 * ks + h]), dsc[ks]);
       }
-      v16f sc_ = score_tile(c & 1, t);
+      return dp_;
+    };
+    // d_qk, d_v <= 128 (no probes): the next tile's dP^ products go to the matrix core between
+    // this tile's S products and its FP32 work, so that work waits less for them (16
+    // more registers; wider heads would spill)
+    constexpr bool PIPE = !PROBE && DQK <= 128 && DV <= 128;
+    v16f dp_nx = v16f{};
+    if constexpr (PIPE) dp_nx = dp_tile(0);
+#pragma unroll
+    for (int t = 0; t < NTL; ++t) {
+      v16f dp, sc_;
+      if constexpr (PIPE) {
+        dp = dp_nx;
+        sc_ = score_tile(c & 1, t);
+        if (t + 1 < NTL) dp_nx = dp_tile(t + 1);
+      } else {
+        dp = dp_tile(t);
+        sc_ = score_tile(c & 1, t);
+      }
       if constexpr (MASK) {
         // key k0 + 32t + 16h + v is visible iff it is <= kmax, i.e. iff v <= lim
         const int lim = kmax - (k0 + 32 * t + 16 * h);

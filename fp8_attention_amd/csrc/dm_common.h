@@ -219,10 +219,13 @@ __device__ __forceinline__ void dma16(const void* g, uint8_t* lds_base) {
 // The same load in the SADDR form: a wave-uniform 64-bit base (SGPRs) plus a
 // 32-bit unsigned per-lane byte offset, so a loop that keeps its per-lane offsets
 // spends no vector instructions on addresses; with a wave-uniform LDS destination
-// the M0 write is scalar too.
+// the M0 write is scalar too.  A vector instruction that writes an SGPR (a lane
+// read) needs five wait states before a memory instruction reads that SGPR, and
+// the compiler cannot see that the assembly reads its base, so the nop provides
+// them whatever instruction wrote the base or M0 last.
 __device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint8_t* lds_base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((lds_void*)lds_base));
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(m0) : "memory");
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(m0) : "memory");
 }
 // wait for this wave's outstanding global loads (including direct-to-LDS ones)
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
