@@ -148,7 +148,8 @@ __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
   };
   auto store_small = [&](uint8_t* st) {
     const bool is_lse = tid < kQT;
-    const float v = smallpad ? (is_lse ? INFINITY : 0.f) : (is_lse ? smallx * kLog2e : smallx);  // padded: P = 0
+    // LSE in log2 units, and delta negated: it is the accumulator input of the dP^ product
+    const float v = smallpad ? (is_lse ? INFINITY : 0.f) : (is_lse ? smallx * kLog2e : -smallx);  // padded: P = 0
     if (tid < 2 * kQT) reinterpret_cast<float*>(st + kLSE)[tid] = v;
   };
 
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
       uint32_t pc[8], dc[8];                       // P^<q>, dS^<q> codes: dword t <-> S tile t
       int kp[2], kd[2];                            // scale exponents of the lane's lo / hi blocks
       const float* lsep = reinterpret_cast<const float*>(st + kLSE) + 16 * g;
-      const float* delp = lsep + kQT;
+      const float* ndelp = lsep + kQT;               // -delta
       const float* qcsp = reinterpret_cast<const float*>(st + kQCS) + 4 * n + g;
       const float* docsp = reinterpret_cast<const float*>(st + kDOCS) + 4 * n + g;
       // S and dP^ of tile t (and the next step's direct load that goes with it)
@@ -199,7 +200,9 @@ __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
         const v8i aq = cat(lds_read16(st + kQC + 2048 * t + ra0), lds_read16(st + kQC + 2048 * t + ra1));
         s = mfma16<E4M3, E4M3>(aq, kb, v4f{}, e8m0(qcsp[64 * t]), ksc);
         const v8i ad = cat(lds_read16(st + kDOC + 2048 * t + ra0), lds_read16(st + kDOC + 2048 * t + ra1));
-        dp = mfma16<E5M2, E4M3>(ad, vb, v4f{}, e8m0(docsp[64 * t]), vsc);
+        // dP^ - delta: the product accumulates onto -delta of the tile's four query rows
+        const v4f nd4 = *reinterpret_cast<const v4f*>(ndelp + 64 * (t >> 2) + 4 * (t & 3));
+        dp = mfma16<E5M2, E4M3>(ad, vb, nd4, e8m0(docsp[64 * t]), vsc);
       };
       // software pipeline: the products of tile t+1 are issued before the FP32 work on
       // tile t, so that work does not wait for the matrix core
@@ -215,7 +218,6 @@ __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
           const v4f s = s_nx, dp = dp_nx;
           if (t + 1 < 8) tile_mm(t + 1, s_nx, dp_nx);
           const v4f l4 = *reinterpret_cast<const v4f*>(lsep + 64 * hf + 4 * tt);
-          const v4f d4 = *reinterpret_cast<const v4f*>(delp + 64 * hf + 4 * tt);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             float x = s[i];
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
             }
             const float p = __builtin_amdgcn_exp2f(fmaf(x, c2, -l4[i]));
             pv[4 * tt + i] = p;
-            sv[4 * tt + i] = p * (dp[i] - d4[i]);
+            sv[4 * tt + i] = p * dp[i];
           }
         }
         // block maxima: the lane's 16 values and its partner's (l ^ 16) form one 32-query block
