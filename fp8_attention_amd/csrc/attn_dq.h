@@ -185,6 +185,11 @@ __global__ __launch_bounds__((64 * dq_waves<PROBE, DQK, DV>())) void dq_kernel(
   const float c2 = sigma * kLog2e;
   const float l2 = (live && qi < L) ? lse[qhead * L + qi] * kLog2e : INFINITY;   // pad rows: P = 0
   const float del = (live && qi < L) ? delta[qhead * L + qi] : 0.f;
+  // -delta in every accumulator slot: the dP^ products of the narrow-head instances start
+  // from it, so dP^ - delta comes out of the matrix core (one rounding instead of two)
+  v16f ndel16;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) ndel16[v] = -del;
   double rsum = 0.0, rabs = 0.0, rcast = 0.0;   // probes: FP32 per chunk, FP64 across chunks
   v16f acc[NCT];
 #pragma unroll
@@ -218,10 +223,11 @@ __global__ __launch_bounds__((64 * dq_waves<PROBE, DQK, DV>())) void dq_kernel(
     v8i dsb[NST];
     int dssc[NST] = {};
     float csum = 0.f, cabs = 0.f, ccast = 0.f;
+    constexpr bool PIPE = !PROBE && DQK <= 128 && DV <= 128;
     // dP^T tile t of chunk c
     auto dp_tile = [&](int t) -> v16f {
       const float* vsr = reinterpret_cast<const float*>(vp + C::OFF_VS) + (32 * t + kr) * VB;
-      v16f dp_ = v16f{};
+      v16f dp_ = PIPE ? ndel16 : v16f{};             // PIPE: the product accumulates onto -delta
 #pragma unroll
       for (int ks = 0; ks < VS; ++ks) {
         const uint8_t* p = vp + 32 * t * DV;
@@ -233,7 +239,6 @@ __global__ __launch_bounds__((64 * dq_waves<PROBE, DQK, DV>())) void dq_kernel(
     // d_qk, d_v <= 128 (no probes): the next tile's dP^ products go to the matrix core between
     // this tile's S products and its FP32 work, so that work waits less for them (16
     // more registers; wider heads would spill)
-    constexpr bool PIPE = !PROBE && DQK <= 128 && DV <= 128;
     v16f dp_nx = v16f{};
     if constexpr (PIPE) dp_nx = dp_tile(0);
 #pragma unroll
@@ -258,7 +263,7 @@ __global__ __launch_bounds__((64 * dq_waves<PROBE, DQK, DV>())) void dq_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const float p = __builtin_amdgcn_exp2f(fmaf(sc_[v], c2, -l2));
-        d[v] = p * (dp[v] - del);
+        d[v] = PIPE ? p * dp[v] : p * (dp[v] - del);
         if constexpr (PROBE) {
           csum += d[v];
           cabs += fabsf(p * dp[v]);
