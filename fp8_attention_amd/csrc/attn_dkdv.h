@@ -185,7 +185,7 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
         x = q < L ? lse[qhead * L + q] * kLog2e : INFINITY;    // padded queries: P = 0
       } else if (e < C::NSMALL) {
         const int q = q0 + e - DQK * 2 - DV * 2 - kBQ;
-        x = q < L ? delta[qhead * L + q] : 0.f;
+        x = q < L ? -delta[qhead * L + q] : 0.f;            // negated: the dP^ products start from it
       }
       smallv[i] = x;
     }
@@ -299,6 +299,9 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
         const uint8_t* qt = st + C::QC + 32 * j * DQK;
         const float* qsr = reinterpret_cast<const float*>(st + C::QCS) + (32 * j + R) * KB;
         v16f s = v16f{}, dp = v16f{};
+        // lane (key R, h), register v <-> step query 32j + 16h + v
+        const float* l2p = reinterpret_cast<const float*>(st + C::LSE) + 32 * j + 16 * h;
+        const float* ndlp = reinterpret_cast<const float*>(st + C::DEL) + 32 * j + 16 * h;   // -delta
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const v8i a = cat(lds_read16(qt + oq[ks][0]), lds_read16(qt + oq[ks][1]));
@@ -307,15 +310,17 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
         if constexpr (DK) {
           const uint8_t* dt = st + C::DOC + 32 * j * DV;
           const float* dsr = reinterpret_cast<const float*>(st + C::DOCS) + (32 * j + R) * VB;
+          // dP^ - delta comes out of the products (not for d_qk = 192: no registers to spare)
+          if constexpr (DQK != 192) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) dp[v] = ndlp[v];
+          }
 #pragma unroll
           for (int ks = 0; ks < VS; ++ks) {
             const v8i a = cat(lds_read16(dt + od[ks][0]), lds_read16(dt + od[ks][1]));
             dp = mfma<E5M2, E4M3>(a, vb[ks], dp, e8m0(dsr[2 * ks + h]), vsc[ks]);
           }
         }
-        // lane (key R, h), register v <-> step query 32j + 16h + v
-        const float* l2p = reinterpret_cast<const float*>(st + C::LSE) + 32 * j + 16 * h;
-        const float* dlp = reinterpret_cast<const float*>(st + C::DEL) + 32 * j + 16 * h;
         if (need_mask) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
@@ -345,12 +350,11 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const v4f l4 = *reinterpret_cast<const v4f*>(l2p + 4 * g);
-            const v4f d4 = *reinterpret_cast<const v4f*>(dlp + 4 * g);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int v = 4 * g + e;
               const float p = __builtin_amdgcn_exp2f(fmaf(s[v], c2, -l4[e]));
-              const float d = p * (dp[v] - d4[e]);
+              const float d = DQK != 192 ? p * dp[v] : p * (dp[v] + ndlp[v]);
               dp[v] = d;                            // dp now holds dS
               am = fmaxf(am, fabsf(d));
             }
