@@ -19,7 +19,8 @@ DM_DELTA_STALE, DM_DELTA_DO_MATCHED, DM_DELTA_MATCHED = 0, 1, 2
 
 # every symbol include/dm_attn.h declares
 EXPORTS = ("dm_padded_len", "dm_status_string", "dm_quantize_blockfp8", "dm_attn_fwd", "dm_attn_delta",
-           "dm_attn_bwd", "dm_attn_bwd_dkdv", "dm_attn_bwd_dq", "dm_attn_bwd_dq_probes")
+           "dm_attn_bwd", "dm_attn_bwd_dkdv", "dm_attn_bwd_dkdv_probes", "dm_attn_bwd_dq", "dm_attn_bwd_dq_probes")
+DM_MAX_SEQLEN = 1 << 24
 
 
 class Operand(ctypes.Structure):
@@ -65,6 +66,8 @@ def load() -> ctypes.CDLL:
     lib.dm_attn_bwd.restype = i32
     lib.dm_attn_bwd_dkdv.argtypes = [sp] + [Operand] * 6 + [vp] * 4 + [vp]
     lib.dm_attn_bwd_dkdv.restype = i32
+    lib.dm_attn_bwd_dkdv_probes.argtypes = [sp] + [Operand] * 6 + [vp] * 6 + [vp]
+    lib.dm_attn_bwd_dkdv_probes.restype = i32
     lib.dm_attn_bwd_dq.argtypes = [sp] + [Operand] * 5 + [vp] * 5 + [vp]
     lib.dm_attn_bwd_dq.restype = i32
     lib.dm_attn_bwd_dq_probes.argtypes = [sp] + [Operand] * 5 + [vp] * 6 + [vp]

@@ -242,21 +242,32 @@ def attn_bwd(shape: AttnShape, ops: dict, lse: torch.Tensor, delta: torch.Tensor
 
 
 def attn_bwd_dkdv(shape: AttnShape, ops: dict, lse: torch.Tensor, delta: torch.Tensor,
-                  dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None) -> dict:
-    """dm_attn_bwd_dkdv -> {"dk","dv"} float32 (the key-stationary half of dm_attn_bwd)."""
+                  dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None, probe: bool = False) -> dict:
+    """dm_attn_bwd_dkdv -> {"dk","dv"} float32 (the key-stationary half of dm_attn_bwd).
+
+    With ``probe`` (dm_attn_bwd_dkdv_probes) also "rowsum" and "rowabs" [B,Hq,L] float64: the
+    row sums of the dS this kernel casts, before the cast, and of |P dP^|."""
     _need_bwd(shape, ops, ("q_c", "q_s", "k_c", "v_c", "do_c", "do_s"), lse, delta, dk=dk, dv=dv)
     dev = lse.device
-    B, Hkv, L = shape.batch, shape.heads_kv, shape.seqlen
+    B, Hq, Hkv, L = shape.batch, shape.heads_q, shape.heads_kv, shape.seqlen
     if dk is None:
         dk = torch.empty((B, Hkv, L, shape.d_qk), dtype=torch.float32, device=dev)
     if dv is None:
         dv = torch.empty((B, Hkv, L, shape.d_v), dtype=torch.float32, device=dev)
     cs = shape.c()
-    st = _lib.load().dm_attn_bwd_dkdv(ctypes.byref(cs), ops["q_c"].c(), ops["q_s"].c(), ops["k_c"].c(),
-                                      ops["v_c"].c(), ops["do_c"].c(), ops["do_s"].c(), lse.data_ptr(),
-                                      delta.data_ptr(), dk.data_ptr(), dv.data_ptr(), _stream(lse))
-    _lib.check(st, "dm_attn_bwd_dkdv")
-    return {"dk": dk, "dv": dv}
+    args = (ctypes.byref(cs), ops["q_c"].c(), ops["q_s"].c(), ops["k_c"].c(), ops["v_c"].c(), ops["do_c"].c(),
+            ops["do_s"].c(), lse.data_ptr(), delta.data_ptr(), dk.data_ptr(), dv.data_ptr())
+    out = {"dk": dk, "dv": dv}
+    if probe:
+        ps = torch.empty((B, Hq, L), dtype=torch.float64, device=dev)
+        pa = torch.empty((B, Hq, L), dtype=torch.float64, device=dev)
+        st = _lib.load().dm_attn_bwd_dkdv_probes(*args, ps.data_ptr(), pa.data_ptr(), _stream(lse))
+        _lib.check(st, "dm_attn_bwd_dkdv_probes")
+        out["rowsum"], out["rowabs"] = ps, pa
+    else:
+        st = _lib.load().dm_attn_bwd_dkdv(*args, _stream(lse))
+        _lib.check(st, "dm_attn_bwd_dkdv")
+    return out
 
 
 def attn_bwd_dq(shape: AttnShape, ops: dict, lse: torch.Tensor, delta: torch.Tensor, probe: bool = False,

@@ -1,4 +1,9 @@
-"""Build libdm.so (the gfx950 HIP kernels and the C ABI) in-tree with hipcc."""
+"""Build libdm.so (the gfx950 HIP kernels and the C ABI) in-tree with hipcc.
+
+Also builds the test-only probe of the FP8 matrix instructions
+(tests/hip/libmfma_acc.so), which the GPU tests use to measure how the
+instructions the kernels rely on accumulate; it is not part of libdm.
+"""
 from __future__ import annotations
 
 import concurrent.futures as cf
@@ -42,6 +47,21 @@ def _compile(src: str) -> str:
     return obj
 
 
+PROBE_SRC = os.path.join(ROOT, "tests", "hip", "mfma_acc.hip")
+PROBE_LIB = os.path.join(ROOT, "tests", "hip", "libmfma_acc.so")
+
+
+def build_probe() -> str:
+    """The test-only instruction probe (tests/hip/mfma_acc.hip -> tests/hip/libmfma_acc.so)."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-shared", PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PROBE_SRC}:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
@@ -52,8 +72,9 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_probe()
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

@@ -13,7 +13,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 dm_status check_shape(const dm_attn_shape* s) {
   if (!s) return DM_ERR_NULL;
   if (s->batch < 1 || s->heads_q < 1 || s->heads_kv < 1 || s->seqlen < 0) return DM_ERR_SHAPE;
-  if (s->batch > 65535 || s->heads_q > 65535 || s->seqlen > (1 << 26)) return DM_ERR_SHAPE;
+  // per-lane load offsets within one head are 32-bit (up to 128 rows of Lp bytes)
+  if (s->batch > 65535 || s->heads_q > 65535 || s->seqlen > DM_MAX_SEQLEN) return DM_ERR_SHAPE;
   if (s->heads_q % s->heads_kv != 0) return DM_ERR_SHAPE;
   // every kernel grid is one-dimensional over (sequence tile of 128, head, batch)
   if ((int64_t)s->batch * s->heads_q * ((s->seqlen + 127) / 128) > INT32_MAX) return DM_ERR_SHAPE;
@@ -155,7 +156,22 @@ dm_status dm_attn_bwd_dkdv(const dm_attn_shape* shape, dm_fp8_operand q_c, dm_fp
   if ((st = check_ptrs({lse, delta, dk, dv})) != DM_OK) return st;
   if (shape->seqlen == 0) return DM_OK;
   return hip_status(dm::launch_dkdv(dims_of(shape), op(q_c), op(q_s), op(k_c), op(v_c), op(do_c), op(do_s), lse,
-                                    delta, dk, dv, stream));
+                                    delta, dk, dv, nullptr, nullptr, stream));
+}
+
+dm_status dm_attn_bwd_dkdv_probes(const dm_attn_shape* shape, dm_fp8_operand q_c, dm_fp8_operand q_s,
+                                  dm_fp8_operand k_c, dm_fp8_operand v_c, dm_fp8_operand do_c, dm_fp8_operand do_s,
+                                  const float* lse, const float* delta, float* dk, float* dv, double* probe_rowsum_ds,
+                                  double* probe_rowsum_abs_pdp, hipStream_t stream) {
+  dm_status st = check_shape(shape);
+  if (st != DM_OK) return st;
+  const dm_fp8_operand ops[6] = {q_c, q_s, k_c, v_c, do_c, do_s};
+  for (const auto& x : ops)
+    if ((st = check_operand(x)) != DM_OK) return st;
+  if ((st = check_ptrs({lse, delta, dk, dv, probe_rowsum_ds, probe_rowsum_abs_pdp})) != DM_OK) return st;
+  if (shape->seqlen == 0) return DM_OK;
+  return hip_status(dm::launch_dkdv(dims_of(shape), op(q_c), op(q_s), op(k_c), op(v_c), op(do_c), op(do_s), lse,
+                                    delta, dk, dv, probe_rowsum_ds, probe_rowsum_abs_pdp, stream));
 }
 
 dm_status dm_attn_bwd_dq(const dm_attn_shape* shape, dm_fp8_operand q_c, dm_fp8_operand k_c, dm_fp8_operand k_s,

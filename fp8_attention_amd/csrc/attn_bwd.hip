@@ -5,22 +5,27 @@
 namespace dm {
 
 hipError_t launch_dkdv(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand vc, Operand doc, Operand dos,
-                       const float* lse, const float* delta, float* dk, float* dv, hipStream_t s) {
-  if (d.dqk == 64 && d.dv == 64) launch_dkdv_t<64, 64>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);
-  else if (d.dqk == 128 && d.dv == 128) return launch_dkdv_d128(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);
-  else if (d.dqk == 192 && d.dv == 128) launch_dkdv_t<192, 128>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);
-  else if (d.dqk == 64 && d.dv == 128) launch_dkdv_t<64, 128>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);
-  else if (d.dqk == 128 && d.dv == 64) launch_dkdv_t<128, 64>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);
-  else if (d.dqk == 192 && d.dv == 64) launch_dkdv_t<192, 64>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);
-  else if (d.dqk == 256 && d.dv == 256) return launch_dkdv_256_256(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+                       const float* lse, const float* delta, float* dk, float* dv, double* ps, double* pa,
+                       hipStream_t s) {
+  if (d.dqk == 64 && d.dv == 64) return launch_dkdv_t<64, 64>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, ps, pa, s);
+  if (d.dqk == 128 && d.dv == 128) return launch_dkdv_d128(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, ps, pa, s);
+  if (d.dqk == 192 && d.dv == 128)
+    return launch_dkdv_t<192, 128>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, ps, pa, s);
+  if (d.dqk == 64 && d.dv == 128)
+    return launch_dkdv_t<64, 128>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, ps, pa, s);
+  if (d.dqk == 128 && d.dv == 64)
+    return launch_dkdv_t<128, 64>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, ps, pa, s);
+  if (d.dqk == 192 && d.dv == 64)
+    return launch_dkdv_t<192, 64>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, ps, pa, s);
+  if (d.dqk == 256 && d.dv == 256)
+    return launch_dkdv_256_256(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, ps, pa, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand ks, Operand vc, Operand doc,
                       Operand dos, const float* lse, const float* delta, float* dq, float* dk, float* dv,
                       double* ps, double* pa, hipStream_t s) {
-  hipError_t e = launch_dkdv(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);
+  hipError_t e = launch_dkdv(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, nullptr, nullptr, s);
   if (e != hipSuccess) return e;
   return launch_dq(d, qc, kc, ks, vc, doc, lse, delta, dq, ps, pa, nullptr, s);
 }

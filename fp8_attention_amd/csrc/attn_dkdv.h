@@ -22,6 +22,12 @@
 // and dV accumulate in registers over every query head of the group and are
 // written once (no atomics).  dQ is computed by the query-stationary kernel in
 // attn_dq.h.
+//
+// The PROBE instance runs the same arithmetic and its dK waves also return, per
+// query row, the sum over keys of the FP32 dS they cast and of |P dP^| (the
+// zero-row-sum property of matched delta, section 03 of the Delta-Matching
+// project page), reduced across the wave's 32 keys and added to the caller's FP64
+// rows atomically.
 #pragma once
 #include <type_traits>
 
@@ -69,14 +75,14 @@ struct DkdvCfg {
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int DQK, int DV, bool CAUSAL>
+template <int DQK, int DV, bool CAUSAL, bool PROBE>
 __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
     const uint8_t* __restrict__ qc, const float* __restrict__ qcs, const uint8_t* __restrict__ qs,
     const float* __restrict__ qss, const uint8_t* __restrict__ kc, const float* __restrict__ kcs,
     const uint8_t* __restrict__ vc, const float* __restrict__ vcs, const uint8_t* __restrict__ doc,
     const float* __restrict__ docs, const uint8_t* __restrict__ dos, const float* __restrict__ doss,
     const float* __restrict__ lse, const float* __restrict__ delta, float* __restrict__ dk, float* __restrict__ dv,
-    int Hq, int Hkv, int L, int Lp, float sigma) {
+    double* __restrict__ psum, double* __restrict__ pabs, int Hq, int Hkv, int L, int Lp, float sigma) {
   using C = DkdvCfg<DQK, DV>;
   constexpr int NW = C::NW, NT = C::NT, KT = C::KT, KB = C::KB, VB = C::VB;
   constexpr int KS = DQK / 64, VS = DV / 64, NKT = DQK / 32, NVT = DV / 32;
@@ -347,6 +353,7 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
           for (int g = 0; g < 4; ++g) code[j][g] = (int)pack4s<E4M3>(s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3], sc);
           scl[j] = k + 127;
         } else {
+          float av[PROBE ? 16 : 1];                 // probe: |P dP^|
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const v4f l4 = *reinterpret_cast<const v4f*>(l2p + 4 * g);
@@ -355,8 +362,24 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
               const int v = 4 * g + e;
               const float p = __builtin_amdgcn_exp2f(fmaf(s[v], c2, -l4[e]));
               const float d = DQK != 192 ? p * dp[v] : p * (dp[v] + ndlp[v]);
+              if constexpr (PROBE) av[v] = fabsf(p * (DQK != 192 ? dp[v] - ndlp[v] : dp[v]));
               dp[v] = d;                            // dp now holds dS
               am = fmaxf(am, fabsf(d));
+            }
+          }
+          if constexpr (PROBE) {
+            // sums over the wave's 32 keys (lanes R of half h); lane R < 16 then holds those
+            // of query 32j + 16h + R of the step
+            float rs[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) rs[v] = dp[v];
+            const float r = group_sum_scatter<16, 32>(rs, lane);
+            const float a = group_sum_scatter<16, 32>(av, lane);
+            const int q = q0 + 32 * j + 16 * h + R;
+            if (R < 16 && q < L) {
+              const int64_t row = (qhead0 + hh) * L + q;
+              unsafeAtomicAdd(psum + row, (double)r);
+              unsafeAtomicAdd(pabs + row, (double)a);
             }
           }
           am = pair_max(am);
@@ -432,18 +455,30 @@ __global__ __launch_bounds__((DkdvCfg<DQK, DV>::NT)) void dkdv_kernel(
 }
 
 template <int DQK, int DV>
-inline void launch_dkdv_t(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand vc, Operand doc,
-                          Operand dos, const float* lse, const float* delta, float* dk, float* dv, hipStream_t s) {
+inline hipError_t launch_dkdv_t(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand vc, Operand doc,
+                                Operand dos, const float* lse, const float* delta, float* dk, float* dv, double* ps,
+                                double* pa, hipStream_t s) {
   using C = DkdvCfg<DQK, DV>;
+  if ((ps == nullptr) != (pa == nullptr)) return hipErrorInvalidValue;
   dim3 grid((unsigned)((d.Lp + C::KT - 1) / C::KT) * d.Hkv * d.B);
-  if (d.causal)
-    hipLaunchKernelGGL((dkdv_kernel<DQK, DV, true>), grid, dim3(C::NT), 0, s, qc.codes, qc.scales, qs.codes,
-                       qs.scales, kc.codes, kc.scales, vc.codes, vc.scales, doc.codes, doc.scales, dos.codes,
-                       dos.scales, lse, delta, dk, dv, d.Hq, d.Hkv, d.L, d.Lp, d.sigma);
-  else
-    hipLaunchKernelGGL((dkdv_kernel<DQK, DV, false>), grid, dim3(C::NT), 0, s, qc.codes, qc.scales, qs.codes,
-                       qs.scales, kc.codes, kc.scales, vc.codes, vc.scales, doc.codes, doc.scales, dos.codes,
-                       dos.scales, lse, delta, dk, dv, d.Hq, d.Hkv, d.L, d.Lp, d.sigma);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(C::NT), 0, s, qc.codes, qc.scales, qs.codes, qs.scales, kc.codes, kc.scales,
+                       vc.codes, vc.scales, doc.codes, doc.scales, dos.codes, dos.scales, lse, delta, dk, dv, ps, pa,
+                       d.Hq, d.Hkv, d.L, d.Lp, d.sigma);
+  };
+  if (ps) {
+    // the probe rows are sums over every key tile: start them from zero
+    const int64_t bytes = (int64_t)d.B * d.Hq * d.L * (int64_t)sizeof(double);
+    hipError_t e = launch_fill_zero(ps, bytes, s);
+    if (e == hipSuccess) e = launch_fill_zero(pa, bytes, s);
+    if (e != hipSuccess) return e;
+    if (d.causal) go(dkdv_kernel<DQK, DV, true, true>);
+    else go(dkdv_kernel<DQK, DV, false, true>);
+  } else {
+    if (d.causal) go(dkdv_kernel<DQK, DV, true, false>);
+    else go(dkdv_kernel<DQK, DV, false, false>);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace dm

@@ -22,6 +22,12 @@
 // buffer by direct global->LDS loads issued during step i, one per S tile (issued
 // all at once, they stall the waves behind them); LSE and delta come through registers.  One barrier per step.  dK and dV accumulate in
 // registers over every query head of the group and are written once.
+//
+// The PROBE instance runs the same arithmetic and also returns, per query row,
+// the sum over keys of the FP32 dS it casts and of |P dP^| (section 03 of the
+// Delta-Matching project page: matched delta makes the rows of dS sum to zero up
+// to FP32 rounding before the cast).  Each wave reduces its 16 keys across lanes
+// and adds its partial sums to the caller's FP64 rows atomically.
 #include <type_traits>
 
 #include "dm_common.h"
@@ -53,14 +59,14 @@ __device__ __forceinline__ int qrow(int t, int m) { return 64 * (t >> 2) + 16 * 
 
 }  // namespace
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool PROBE>
 __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
     const uint8_t* __restrict__ qc, const float* __restrict__ qcs, const uint8_t* __restrict__ qs,
     const float* __restrict__ qss, const uint8_t* __restrict__ kc, const float* __restrict__ kcs,
     const uint8_t* __restrict__ vc, const float* __restrict__ vcs, const uint8_t* __restrict__ doc,
     const float* __restrict__ docs, const uint8_t* __restrict__ dos, const float* __restrict__ doss,
     const float* __restrict__ lse, const float* __restrict__ delta, float* __restrict__ dk, float* __restrict__ dv,
-    int Hq, int Hkv, int L, int Lp, float sigma) {
+    double* __restrict__ psum, double* __restrict__ pabs, int Hq, int Hkv, int L, int Lp, float sigma) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kSTAGE];
 
   const int tid = threadIdx.x;
@@ -212,6 +218,7 @@ __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
       for (int hf = 0; hf < 2; ++hf) {
         // tiles 4hf .. 4hf+3: lane (n, g) holds queries 64hf + 16g + 4tt + i
         float pv[16], sv[16];
+        float av[PROBE ? 16 : 1];                  // probe: |P dP^| (dP^ = the accumulator plus delta)
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
           const int t = 4 * hf + tt;
@@ -228,6 +235,25 @@ __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
             const float p = __builtin_amdgcn_exp2f(fmaf(x, c2, -l4[i]));
             pv[4 * tt + i] = p;
             sv[4 * tt + i] = p * dp[i];
+            if constexpr (PROBE) {
+              const v4f n4 = *reinterpret_cast<const v4f*>(ndelp + 64 * hf + 4 * tt);
+              av[4 * tt + i] = fabsf(p * (dp[i] - n4[i]));
+            }
+          }
+        }
+        if constexpr (PROBE) {
+          // sums over the wave's 16 keys (the 16 lanes of group g); lane n then holds
+          // those of query 64hf + 16g + n and adds them to the row totals
+          float rs[16];
+#pragma unroll
+          for (int k = 0; k < 16; ++k) rs[k] = sv[k];
+          const float r = group_sum_scatter<16, 16>(rs, lane);
+          const float a = group_sum_scatter<16, 16>(av, lane);
+          const int q = q0 + 64 * hf + 16 * g + n;
+          if (q < L) {
+            const int64_t row = (qhead0 + hh) * L + q;
+            unsafeAtomicAdd(psum + row, (double)r);
+            unsafeAtomicAdd(pabs + row, (double)a);
           }
         }
         // block maxima: the lane's 16 values and its partner's (l ^ 16) form one 32-query block
@@ -303,17 +329,27 @@ __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
 }
 
 hipError_t launch_dkdv_d128(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand vc, Operand doc,
-                            Operand dos, const float* lse, const float* delta, float* dk, float* dv, hipStream_t s) {
-  if (d.dqk != kD || d.dv != kD || d.Lp % kKT != 0) return hipErrorInvalidValue;
+                            Operand dos, const float* lse, const float* delta, float* dk, float* dv, double* ps,
+                            double* pa, hipStream_t s) {
+  if (d.dqk != kD || d.dv != kD || d.Lp % kKT != 0 || (ps == nullptr) != (pa == nullptr)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(d.Lp / kKT) * d.Hkv * d.B);
-  if (d.causal)
-    hipLaunchKernelGGL(dkdv_d128_kernel<true>, grid, dim3(kNT), 0, s, qc.codes, qc.scales, qs.codes, qs.scales,
-                       kc.codes, kc.scales, vc.codes, vc.scales, doc.codes, doc.scales, dos.codes, dos.scales, lse,
-                       delta, dk, dv, d.Hq, d.Hkv, d.L, d.Lp, d.sigma);
-  else
-    hipLaunchKernelGGL(dkdv_d128_kernel<false>, grid, dim3(kNT), 0, s, qc.codes, qc.scales, qs.codes, qs.scales,
-                       kc.codes, kc.scales, vc.codes, vc.scales, doc.codes, doc.scales, dos.codes, dos.scales, lse,
-                       delta, dk, dv, d.Hq, d.Hkv, d.L, d.Lp, d.sigma);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(kNT), 0, s, qc.codes, qc.scales, qs.codes, qs.scales, kc.codes, kc.scales,
+                       vc.codes, vc.scales, doc.codes, doc.scales, dos.codes, dos.scales, lse, delta, dk, dv, ps, pa,
+                       d.Hq, d.Hkv, d.L, d.Lp, d.sigma);
+  };
+  if (ps) {
+    // the probe rows are sums over every key tile: start them from zero
+    const int64_t bytes = (int64_t)d.B * d.Hq * d.L * (int64_t)sizeof(double);
+    hipError_t e = launch_fill_zero(ps, bytes, s);
+    if (e == hipSuccess) e = launch_fill_zero(pa, bytes, s);
+    if (e != hipSuccess) return e;
+    if (d.causal) go(dkdv_d128_kernel<true, true>);
+    else go(dkdv_d128_kernel<false, true>);
+  } else {
+    if (d.causal) go(dkdv_d128_kernel<true, false>);
+    else go(dkdv_d128_kernel<false, false>);
+  }
   return hipGetLastError();
 }
 

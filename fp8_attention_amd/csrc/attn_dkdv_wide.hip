@@ -5,10 +5,9 @@
 namespace dm {
 
 hipError_t launch_dkdv_256_256(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand vc, Operand doc,
-                               Operand dos, const float* lse, const float* delta, float* dk, float* dv,
-                               hipStream_t s) {
-  launch_dkdv_t<256, 256>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, s);
-  return hipGetLastError();
+                               Operand dos, const float* lse, const float* delta, float* dk, float* dv, double* ps,
+                               double* pa, hipStream_t s) {
+  return launch_dkdv_t<256, 256>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, ps, pa, s);
 }
 
 }  // namespace dm

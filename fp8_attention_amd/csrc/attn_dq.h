@@ -1,7 +1,6 @@
 // dQ of block-scaled FP8 attention (query-stationary), with the row-sum probes.
 //
-// Workgroup = 8 waves = 256 queries (32 per wave; 4 waves when the probes are on
-// or d_qk + d_v > 256);
+// Workgroup = 8 waves = 256 queries (32 per wave; 4 waves when d_qk + d_v > 256);
 // a 1-D grid over (query tile, Hq, B) with the query tile slowest, so the longest
 // causal tiles start first.
 // The wave's Q^<c> and dO^<c> rows sit in registers as the B operands of
@@ -12,7 +11,10 @@
 // blocks in registers (the lane pair holds a whole block) and is already the B
 // operand of dQ^T += K^<s>^T dS^<k>^T.  Each dQ row is written once, so dQ needs
 // no atomics and is bitwise deterministic.  The pre-cast row sums of dS and of
-// |P dP^| (the probes) are plain register sums here.
+// |P dP^| (the probes) are plain register sums here; the PROBE instance runs the
+// arithmetic of the plain one unchanged (same waves, same products, same casts),
+// so its dQ is bit for bit the plain instance's and its sums are those of the dS
+// that instance casts.
 // K^<c>, V^<c> and K^<s> chunks arrive in double-buffered LDS by direct
 // global->LDS loads issued one chunk ahead; one barrier per chunk.
 #pragma once
@@ -23,11 +25,10 @@
 
 namespace dm {
 
-// waves per workgroup (32 queries each): 8 (two per SIMD); the probe variant, with
-// its extra row sums live, and head dims beyond d_qk + d_v = 256 (192/128: spills at
-// two waves per SIMD and runs 25% faster at one; 256/256) run one wave per SIMD with
-// the full register file (accumulators in AGPRs)
-template <bool PROBE, int DQK, int DV> constexpr int dq_waves() { return (PROBE || DQK + DV > 256) ? 4 : 8; }
+// waves per workgroup (32 queries each): 8 (two per SIMD); head dims beyond
+// d_qk + d_v = 256 (192/128: spills at two waves per SIMD and runs 25% faster at one;
+// 256/256) run one wave per SIMD with the full register file (accumulators in AGPRs)
+template <int DQK, int DV> constexpr int dq_waves() { return DQK + DV > 256 ? 4 : 8; }
 // keys per LDS chunk: 128, or 64 when d_qk = d_v = 256 (two chunks of K^<c>, V^<c>
 // and K^<s> at 128 keys would not fit in LDS)
 template <int DQK, int DV> constexpr int dq_chunk() { return DQK + DV > 384 ? 64 : 128; }
@@ -51,7 +52,7 @@ struct DqLds {
 };
 
 template <int DQK, int DV, bool CAUSAL, bool PROBE>
-__global__ __launch_bounds__((64 * dq_waves<PROBE, DQK, DV>())) void dq_kernel(
+__global__ __launch_bounds__((64 * dq_waves<DQK, DV>())) void dq_kernel(
     const uint8_t* __restrict__ qc, const float* __restrict__ qcs, const uint8_t* __restrict__ kc,
     const float* __restrict__ kcs, const uint8_t* __restrict__ vc, const float* __restrict__ vcs,
     const uint8_t* __restrict__ kst, const float* __restrict__ ksts, const uint8_t* __restrict__ doc,
@@ -59,7 +60,7 @@ __global__ __launch_bounds__((64 * dq_waves<PROBE, DQK, DV>())) void dq_kernel(
     float* __restrict__ dq, double* __restrict__ psum, double* __restrict__ pabs, double* __restrict__ pcast, int Hq,
     int Hkv, int L, int Lp,
     float sigma) {
-  constexpr int kDqWaves = dq_waves<PROBE, DQK, DV>(), kDqQ = 32 * kDqWaves;
+  constexpr int kDqWaves = dq_waves<DQK, DV>(), kDqQ = 32 * kDqWaves;
   constexpr int CK = dq_chunk<DQK, DV>(), NTL = CK / 32, NST = CK / 64;   // key tiles, 64-key halves
   using C = DqLds<DQK, DV, kDqWaves, CK>;
   constexpr int KS = DQK / 64, VS = DV / 64, KB = DQK / 32, VB = DV / 32;
@@ -223,7 +224,7 @@ __global__ __launch_bounds__((64 * dq_waves<PROBE, DQK, DV>())) void dq_kernel(
     v8i dsb[NST];
     int dssc[NST] = {};
     float csum = 0.f, cabs = 0.f, ccast = 0.f;
-    constexpr bool PIPE = !PROBE && DQK <= 128 && DV <= 128;
+    constexpr bool PIPE = DQK <= 128 && DV <= 128;
     // dP^T tile t of chunk c
     auto dp_tile = [&](int t) -> v16f {
       const float* vsr = reinterpret_cast<const float*>(vp + C::OFF_VS) + (32 * t + kr) * VB;
@@ -236,7 +237,7 @@ __global__ __launch_bounds__((64 * dq_waves<PROBE, DQK, DV>())) void dq_kernel(
       }
       return dp_;
     };
-    // d_qk, d_v <= 128 (no probes): the next tile's dP^ products go to the matrix core between
+    // d_qk, d_v <= 128: the next tile's dP^ products go to the matrix core between
     // this tile's S products and its FP32 work, so that work waits less for them (16
     // more registers; wider heads would spill)
     v16f dp_nx = v16f{};
@@ -266,7 +267,7 @@ __global__ __launch_bounds__((64 * dq_waves<PROBE, DQK, DV>())) void dq_kernel(
         d[v] = PIPE ? p * dp[v] : p * (dp[v] - del);
         if constexpr (PROBE) {
           csum += d[v];
-          cabs += fabsf(p * dp[v]);
+          cabs += fabsf(p * (PIPE ? dp[v] + del : dp[v]));   // PIPE: dp holds dP^ - delta
         }
         am = fmaxf(am, fabsf(d[v]));
       }
@@ -365,7 +366,7 @@ template <int DQK, int DV, bool CAUSAL, bool PROBE>
 static void launch_dq_t4(const AttnDims& d, Operand qc, Operand kc, Operand ks, Operand vc, Operand doc,
                          const float* lse, const float* delta, float* dq, double* ps, double* pa, double* pc,
                          hipStream_t s) {
-  constexpr int kDqQ = 32 * dq_waves<PROBE, DQK, DV>();
+  constexpr int kDqQ = 32 * dq_waves<DQK, DV>();
   dim3 grid((unsigned)((d.Lp + kDqQ - 1) / kDqQ) * d.Hq * d.B);
   hipLaunchKernelGGL((dq_kernel<DQK, DV, CAUSAL, PROBE>), grid, dim3(2 * kDqQ), 0, s, qc.codes, qc.scales, kc.codes,
                      kc.scales, vc.codes, vc.scales, ks.codes, ks.scales, doc.codes, doc.scales, lse, delta, dq, ps,

@@ -132,6 +132,30 @@ __device__ __forceinline__ float max16(const v16f& x) {
   return fmaxf(m, x[15]);
 }
 
+// Sum of x[0..NV) over each group of W consecutive lanes, scattered: afterwards the
+// lane with (lane % NV) == k holds the group's sum of x[k] (every value of x is
+// overwritten).  A reduce-scatter butterfly: log2(W / NV) full exchanges, then one
+// halving exchange per remaining lane bit, NV - 1 shuffles in all.
+template <int NV, int W>
+__device__ __forceinline__ float group_sum_scatter(float (&x)[NV], int lane) {
+  static_assert(NV >= 1 && NV <= W && (NV & (NV - 1)) == 0 && (W & (W - 1)) == 0 && W <= 64, "powers of two");
+#pragma unroll
+  for (int m = W / 2; m >= NV; m >>= 1)
+#pragma unroll
+    for (int j = 0; j < NV; ++j) x[j] += __shfl_xor(x[j], m, W);
+#pragma unroll
+  for (int m = NV / 2; m >= 1; m >>= 1) {
+    const bool hi = (lane & m) != 0;
+#pragma unroll
+    for (int j = 0; j < m; ++j) {
+      const float send = hi ? x[j] : x[j + m];
+      const float keep = hi ? x[j + m] : x[j];
+      x[j] = keep + __shfl_xor(send, m, W);
+    }
+  }
+  return x[0];
+}
+
 // E8M0 byte of a float32 power-of-two scale (its biased exponent).
 __device__ __forceinline__ int e8m0(float s) { return (int)(__float_as_uint(s) >> 23); }
 

@@ -31,15 +31,20 @@ hipError_t launch_bwd(const AttnDims& d, Operand q_c, Operand q_s, Operand k_c, 
                       Operand do_c, Operand do_s, const float* lse, const float* delta, float* dq, float* dk,
                       float* dv, double* probe_sum, double* probe_abs, hipStream_t s);
 
+// ps, pa: the dK/dV kernel's row-sum probes (pre-cast sum of dS, sum of |P dP^|), both
+// null or both set; they are zeroed and then accumulated over key tiles
 hipError_t launch_dkdv(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand vc, Operand doc, Operand dos,
-                       const float* lse, const float* delta, float* dk, float* dv, hipStream_t s);
+                       const float* lse, const float* delta, float* dk, float* dv, double* ps, double* pa,
+                       hipStream_t s);
 
 // d_qk = d_v = 128 form of launch_dkdv (attn_dkdv128.hip)
 hipError_t launch_dkdv_d128(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand vc, Operand doc,
-                            Operand dos, const float* lse, const float* delta, float* dk, float* dv, hipStream_t s);
+                            Operand dos, const float* lse, const float* delta, float* dk, float* dv, double* ps,
+                            double* pa, hipStream_t s);
 // d_qk = d_v = 256 form of launch_dkdv (attn_dkdv_wide.hip)
 hipError_t launch_dkdv_256_256(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand vc, Operand doc,
-                               Operand dos, const float* lse, const float* delta, float* dk, float* dv, hipStream_t s);
+                               Operand dos, const float* lse, const float* delta, float* dk, float* dv, double* ps,
+                               double* pa, hipStream_t s);
 
 // ps, pa, pc: the row-sum probes (pre-cast sum of dS, sum of |P dP^|, sum of the
 // decoded dS^<k>); ps and pa both null or both set, pc only with them

@@ -44,8 +44,9 @@
  *   Delta-Matching page, section 04 "What changes as the model gets larger?").
  *   Other pairs return DM_ERR_SHAPE.
  *   Hq must be a multiple of Hkv (GQA: query head h reads KV head h/(Hq/Hkv)).
- *   softmax_scale must be positive and finite.  B, Hq, Hkv >= 1 and L >= 0;
- *   L == 0 is a no-op.
+ *   softmax_scale must be positive and finite.  B, Hq, Hkv >= 1 and
+ *   0 <= L <= DM_MAX_SEQLEN (the kernels address up to 128 rows of one head's
+ *   sequence-major operand with 32-bit offsets); L == 0 is a no-op.
  * - Pointers must be 16-byte aligned (DM_ERR_ALIGN otherwise).
  * - Calls are reentrant; the library has no global state.
  */
@@ -58,6 +59,9 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* Largest supported sequence length (2^24). */
+#define DM_MAX_SEQLEN (1 << 24)
 
 typedef enum {
   DM_OK = 0,
@@ -101,8 +105,9 @@ const char* dm_status_string(dm_status s);
  *           rows_out % 32 == 0; codes [batch][cols][rows_out],
  *           scales [batch][cols][rows_out/32].
  *   rows_out >= rows; rows in [rows, rows_out) are written as zero codes with
- *   scale 2^-126.  cols >= 1 and cols % 32 == 0 for DM_AXIS_COLS;
- *   cols >= 1 for DM_AXIS_ROWS.  Output is bit-exact with the rule above.
+ *   scale 2^-126.  On both axes cols must be a positive multiple of 32 (at most
+ *   2^20), batch <= 65535 and rows_out <= 2^36; otherwise DM_ERR_SHAPE.
+ *   Output is bit-exact with the rule above.
  */
 dm_status dm_quantize_blockfp8(const void* x, dm_dtype dtype, int64_t batch, int64_t rows,
                                int64_t cols, int64_t rows_out, dm_block_axis axis,
@@ -181,6 +186,25 @@ dm_status dm_attn_bwd_dq(const dm_attn_shape* shape, dm_fp8_operand q_c, dm_fp8_
                          dm_fp8_operand k_s, dm_fp8_operand v_c, dm_fp8_operand do_c,
                          const float* lse, const float* delta, float* dq,
                          double* probe_rowsum_ds, double* probe_rowsum_abs_pdp, hipStream_t stream);
+
+/*
+ * dm_attn_bwd_dkdv with the row-sum probes of the dS that the dK/dV kernel itself
+ * computes and casts (section 03 "Does matching the backward operands fix it?":
+ * with matched delta the rows of dS sum to zero up to FP32 rounding before dS is
+ * cast to FP8).  dK and dV are bit for bit those of dm_attn_bwd_dkdv.
+ *   probe_rowsum_ds:      [B][Hq][L] double, sum_j dS_ij of the FP32 dS before its
+ *                         E5M2 cast along queries (the dK operand);
+ *   probe_rowsum_abs_pdp: [B][Hq][L] double, sum_j |P_ij dP^_ij|.
+ * Both are required (non-NULL, 16-byte aligned) and fully overwritten: the call
+ * zeroes them, then adds FP32 partial sums over groups of 16 or 32 keys to them
+ * with FP64 atomics, so the last bits may differ from run to run.  Other errors as
+ * for dm_attn_bwd.
+ */
+dm_status dm_attn_bwd_dkdv_probes(const dm_attn_shape* shape, dm_fp8_operand q_c, dm_fp8_operand q_s,
+                                  dm_fp8_operand k_c, dm_fp8_operand v_c, dm_fp8_operand do_c,
+                                  dm_fp8_operand do_s, const float* lse, const float* delta, float* dk,
+                                  float* dv, double* probe_rowsum_ds, double* probe_rowsum_abs_pdp,
+                                  hipStream_t stream);
 
 /*
  * dm_attn_bwd_dq with a third row-sum probe (section 03 "Does matching the

@@ -25,6 +25,11 @@ REL_TOL = 2e-3          # max-abs error <= REL_TOL * RMS(oracle tensor) (+ allow
 NORM_TOL = 1e-3
 ROWSUM_TOL = 1e-5       # |sum_j dS_ij| <= ROWSUM_TOL * sum_j |P_ij dP_ij| under Delta-Matching
 
+# Every comparison's statistics, printed in the session summary (tests/conftest.py),
+# labelled with the running test (set by an autouse fixture there).
+STATS: list = []
+CURRENT_TEST = ""
+
 
 def to64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu", torch.float64).numpy()
@@ -60,7 +65,7 @@ def run_oracle(inputs: dict, shp: A.Shape, modes=("matched",), rows=None, radius
 
 
 def compare(name: str, gpu, ref: np.ndarray, allow=None, rel: float = REL_TOL, mask=None,
-            norm_rel=None, flip=None) -> dict:
+            norm_rel=None, flip=None, case: str = "") -> dict:
     """Assert |gpu - ref| <= rel * RMS(ref) + allow elementwise over finite ref entries.
 
     ``allow`` is the oracle's bound of how far a correct kernel result may sit
@@ -71,6 +76,10 @@ def compare(name: str, gpu, ref: np.ndarray, allow=None, rel: float = REL_TOL, m
     oracle's cast-ambiguity radius (a cast whose exact input lies within the
     kernel's error of a rounding boundary has two correct results; one such flip
     in a short, peaked row moves that row by several percent).
+
+    The returned statistics split the elements beyond ``rel * RMS`` into those
+    the flip radius explains, those the rest of the allowance (the matrix cores'
+    accumulation bound) explains, and the unexplained ones (which fail).
     """
     g = to64(gpu) if isinstance(gpu, torch.Tensor) else np.asarray(gpu, dtype=np.float64)
     ok = np.isfinite(ref)
@@ -86,9 +95,14 @@ def compare(name: str, gpu, ref: np.ndarray, allow=None, rel: float = REL_TOL, m
     nrel = float(np.sqrt(np.sum(err[ok] ** 2)) / refn)
     unexp = err if flip is None else np.maximum(err - np.where(np.isfinite(flip), flip, 0.0), 0.0)
     nrel_u = float(np.sqrt(np.sum(unexp[ok] ** 2)) / refn)
-    stats = {"name": name, "rms": rms, "max_err_over_rms": float(err[ok].max() / max(rms, 1e-300)),
+    fl = 0.0 if flip is None else np.where(np.isfinite(flip), flip, 0.0)
+    beyond = ok & (err > base)
+    by_flip = beyond & (err <= base + fl)
+    stats = {"case": case or CURRENT_TEST, "name": name, "rms": rms, "max_err_over_rms": float(err[ok].max() / max(rms, 1e-300)),
              "norm_rel_err": nrel, "norm_rel_unexplained": nrel_u, "n": int(ok.sum()),
-             "n_beyond_rel_rms": int((ok & (err > base)).sum()), "n_bad": int(bad.sum())}
+             "n_beyond_rel_rms": int(beyond.sum()), "n_flip_explained": int(by_flip.sum()),
+             "n_accumulation_explained": int((beyond & ~by_flip & (err <= tol)).sum()), "n_bad": int(bad.sum())}
+    STATS.append(stats)
     if bad.any():
         idx = np.argwhere(bad)[:5]
         detail = [(tuple(int(i) for i in ix), float(g[tuple(ix)]), float(ref[tuple(ix)]),

@@ -70,12 +70,25 @@ BAD_SHAPES = [
     AttnShape(1, 2, 2, 128, 128, 128, True, -1.0),  # non-positive scale
     AttnShape(1, 2, 2, 128, 128, 128, True, float("nan")),
     AttnShape(1, 2, 2, (1 << 26) + 1, 128, 128, True),
+    AttnShape(1, 2, 2, _lib.DM_MAX_SEQLEN + 1, 128, 128, True),   # beyond the 32-bit load offsets
 ]
 
 
 @pytest.mark.parametrize("shape", BAD_SHAPES)
 def test_bad_shapes(shape):
     assert _fwd(shape) == _lib.DM_ERR_SHAPE
+
+
+def test_longest_sequence_passes_the_shape_check():
+    """L = DM_MAX_SEQLEN is accepted by the shape check (the call then fails on its NULL output,
+    which is checked after the shape), one more is not; the header states the same limit."""
+    longest = AttnShape(1, 2, 2, _lib.DM_MAX_SEQLEN, 128, 128, True)
+    assert _fwd(longest, o=None) == _lib.DM_ERR_NULL
+    assert _fwd(AttnShape(1, 2, 2, _lib.DM_MAX_SEQLEN + 1, 128, 128, True), o=None) == _lib.DM_ERR_SHAPE
+    m = re.search(r"#define DM_MAX_SEQLEN \(1 << (\d+)\)", open(HEADER).read())
+    assert m and (1 << int(m.group(1))) == _lib.DM_MAX_SEQLEN
+    # the d = 128 dK/dV kernel addresses up to 127 channel rows of Lp bytes with 32-bit offsets
+    assert 127 * _lib.DM_MAX_SEQLEN + 128 * 16 < 2 ** 31
 
 
 def test_bad_causal_flag_and_null_shape():
@@ -131,8 +144,14 @@ def test_split_backward_validation():
     assert pr(ctypes.byref(s), *[op] * 5, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == _lib.DM_ERR_NULL
     assert pr(ctypes.byref(s), *[op] * 5, FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == _lib.DM_ERR_NULL
     assert pr(ctypes.byref(s), *[op] * 5, FAKE, FAKE, FAKE, FAKE, FAKE, MIS, None) == _lib.DM_ERR_ALIGN
+    # the dK/dV probe call requires both probe buffers
+    kp = lib.dm_attn_bwd_dkdv_probes
+    assert kp(ctypes.byref(s), *[op] * 6, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == _lib.DM_ERR_NULL
+    assert kp(ctypes.byref(s), *[op] * 6, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == _lib.DM_ERR_NULL
+    assert kp(ctypes.byref(s), *[op] * 6, FAKE, FAKE, FAKE, FAKE, FAKE, MIS, None) == _lib.DM_ERR_ALIGN
     s.d_qk = 96
     assert pr(ctypes.byref(s), *[op] * 5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == _lib.DM_ERR_SHAPE
+    assert kp(ctypes.byref(s), *[op] * 6, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == _lib.DM_ERR_SHAPE
     assert lib.dm_attn_bwd_dkdv(ctypes.byref(s), *[op] * 6, FAKE, FAKE, FAKE, FAKE, None) == _lib.DM_ERR_SHAPE
     assert lib.dm_attn_bwd_dq(ctypes.byref(s), *[op] * 5, FAKE, FAKE, FAKE, None, None, None) == _lib.DM_ERR_SHAPE
 
@@ -144,6 +163,7 @@ def test_quantize_validation():
     assert q(FAKE, 0, 1, 64, 64, 64, 5, 0, FAKE, FAKE, None) == _lib.DM_ERR_ENUM      # axis
     assert q(FAKE, 0, 1, 64, 64, 64, 0, 3, FAKE, FAKE, None) == _lib.DM_ERR_ENUM      # format
     assert q(FAKE, 0, 1, 64, 48, 64, 0, 0, FAKE, FAKE, None) == _lib.DM_ERR_SHAPE     # cols % 32
+    assert q(FAKE, 0, 1, 64, 48, 64, 1, 0, FAKE, FAKE, None) == _lib.DM_ERR_SHAPE     # cols % 32 (rows axis)
     assert q(FAKE, 0, 1, 64, 64, 32, 0, 0, FAKE, FAKE, None) == _lib.DM_ERR_SHAPE     # rows_out < rows
     assert q(FAKE, 0, 1, 64, 64, 80, 1, 0, FAKE, FAKE, None) == _lib.DM_ERR_SHAPE     # rows_out % 32 (rows axis)
     assert q(FAKE, 0, 0, 64, 64, 64, 0, 0, FAKE, FAKE, None) == _lib.DM_ERR_SHAPE     # batch

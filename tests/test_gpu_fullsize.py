@@ -1,23 +1,29 @@
 """GPU parity at the full workload sizes, in the call sequence bench.py times.
 
 The GPU runs the whole problem (quantize, forward, matched delta, dK/dV, dQ on
-preallocated outputs, the same calls as bench.py).  The oracle cannot redo a
-full 8K or 64K problem in reasonable time, so it checks a sample it can compute
-exactly: one batch entry and KV group (the last of each, so the highest head and
-batch offsets are exercised), and within it
+preallocated outputs, the same calls as bench.py).  The oracle checks the part
+of it that it can compute exactly in about a minute: one batch entry and KV
+group (the last of each, so the highest head and batch offsets are exercised),
+and within it
   * FP8 codes and scales of every operand of the group: bit-exact;
-  * O, LSE, delta and dQ on sampled 32-row blocks (the first, the last and a
-    spread of others) plus a tail of the sequence;
-  * dK and dV on the keys of that tail: under causal masking only rows at or
-    after a key reach it, so the tail's rows determine those keys completely.
-The same elementwise and norm-wise bars as the small-size tests apply.  The
-matched-mode row sums |sum_j dS_ij| <= 1e-5 sum_j |P_ij dP_ij| are checked on
-every row of the full problem from the kernel's probe (a property that needs no
-oracle).
+  * at sequence lengths up to 8K: every query row, so O, LSE, delta and dQ are
+    compared on all rows and dK, dV on all keys -- including the first key
+    tiles, whose workgroups walk every query step of every head of the group;
+  * at 64K: O, LSE, delta and dQ on sampled 32-row blocks and on the last 4096
+    rows, and dK, dV on the last 4096 keys (under causal masking only rows at or
+    after a key reach it, so those rows determine the keys completely).
+The same elementwise and norm-wise bars as the small-size tests apply.  On every
+row of the full problem, the matched-mode row sums |sum_j dS_ij| <= 1e-5
+sum_j |P_ij dP_ij| are checked from the probes of both backward kernels (a
+property that needs no oracle), and the probing instances are required to give
+the timed instances' dQ, dK and dV bit for bit.
+
+The oracle runs in up to 16 spawned processes (one BLAS thread each): every
+query head of the group split into row ranges; dK and dV are summed over the
+ranges and heads.
 """
 import concurrent.futures as cf
 import multiprocessing
-import os
 import sys
 import time
 
@@ -31,27 +37,74 @@ from tests import parity_util as U
 
 pytestmark = pytest.mark.gpu
 
-# workload -> (rows of the tail, number of sampled 32-row blocks before it).  The oracle
-# runs one query head per worker process (spawned: no GPU state crosses over).
+# workload -> rows the oracle covers: None (every row), or (tail, number of sampled 32-row
+# blocks before the tail)
 CASES = {
-    "gqa_4k": (256, 4),
-    "gqa_8k": (256, 4),
-    "gqa_64k": (64, 1),
-    "mla_4k": (256, 4),
-    "gqa_d256_4k": (256, 4),
+    "gqa_4k": None,
+    "gqa_8k": None,
+    "gqa_64k": (4096, 8),
+    "mla_4k": None,
+    "gqa_d256_4k": None,
 }
+WORKERS = 16
 
 
 def _log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def _rows(L: int, tail: int, nblocks: int):
-    """32-aligned sampled row ranges: nblocks blocks spread from row 0 to just before
-    the tail, and the tail [L - tail, L)."""
+def _rows(L: int, spec):
+    """32-aligned row ranges the oracle covers, and the first row of the contiguous tail."""
+    if spec is None:
+        return [(0, L)], 0
+    tail, nblocks = spec
     t0 = L - tail
     starts = sorted({int(s) // 32 * 32 for s in np.linspace(0, t0 - 32, nblocks)})
-    return [(s, s + 32) for s in starts] + [(t0, L)]
+    return [(s, s + 32) for s in starts] + [(t0, L)], t0
+
+
+def _split(ranges, parts):
+    """Cut the row ranges into about ``parts`` pieces of similar size (32-aligned)."""
+    total = sum(b - a for a, b in ranges)
+    size = max(32, -(-total // parts) // 32 * 32)
+    out, cur, n = [], [], 0
+    for a, b in ranges:
+        while a < b:
+            take = min(b - a, size - n)
+            cur.append((a, a + take))
+            n += take
+            a += take
+            if n == size:
+                out.append(cur)
+                cur, n = [], 0
+    if cur:
+        out.append(cur)
+    return out
+
+
+def _oracle_part(q, k, v, do, shp, rows, key0, want_codes):
+    """Oracle chain for one query head on some row ranges (run in a worker process).
+
+    Returns the row-wise results on those rows only, dK/dV contributions of those rows
+    to keys [key0, L), and (want_codes) the head's quantized operands."""
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        r = U.oracle_head_chain(q, k, v, do, shp, rows)
+    idx = np.concatenate([np.arange(a, b) for a, b in rows])
+    f, bw = r["fwd"], r["bwd"]
+    out = {"idx": idx}
+    for n in ("o", "r_o", "b_o"):
+        out[n] = f[n][0, 0, idx]
+    for n in ("lse", "b_lse"):
+        out[n] = f[n][0, 0, idx]
+    out["delta"], out["derr"] = r["delta"][0, 0, idx], r["derr"][0, 0, idx]
+    for n in ("dq", "r_dq", "b_dq"):
+        out[n] = bw[n][0, 0, idx]
+    for n in ("dk", "dv", "r_dk", "b_dk", "r_dv", "b_dv"):
+        out[n] = bw[n][0, 0, key0:]
+    if want_codes:
+        out["qops"] = r["qops"]
+    return out
 
 
 @pytest.mark.timeout(1200)
@@ -59,7 +112,6 @@ def _rows(L: int, tail: int, nblocks: int):
 def test_fullsize_chain_sampled(name):
     from fp8_attention_amd import api
     w = W.WORKLOADS[name]
-    tail, nblocks = CASES[name]
     B, Hq, Hkv, L, G = w.batch, w.heads_q, w.heads_kv, w.seqlen, w.group
     _log(f"[fullsize] {name}: {w}")
     inputs = W.generate(w)
@@ -78,44 +130,75 @@ def test_fullsize_chain_sampled(name):
                    lse=lse, out=delta)
     api.attn_bwd_dkdv(shape, ops, lse, delta, dk=dk, dv=dv)
     api.attn_bwd_dq(shape, ops, lse, delta, dq=dq)
-    # the row-sum probe over the whole problem (the probing dQ instance)
-    pr = api.attn_bwd_dq(shape, ops, lse, delta, probe=True)
+    # the row-sum probes of both backward kernels over the whole problem; the probing
+    # instances must reproduce the timed ones bit for bit
+    pq = api.attn_bwd_dq(shape, ops, lse, delta, probe=True)
+    pk = api.attn_bwd_dkdv(shape, ops, lse, delta, probe=True)
     torch.cuda.synchronize()
     _log("   gpu done")
-    rs, ra = U.to64(pr["rowsum"]), U.to64(pr["rowabs"])
-    ratio = np.abs(rs) / np.maximum(ra, 1e-300)
-    assert np.all(np.abs(rs) <= U.ROWSUM_TOL * ra), f"row-sum ratio max {float(ratio.max()):.3e}"
-    _log(f"   row sums: max |sum dS| / sum |P dP| = {float(ratio.max()):.2e} over {rs.size} rows")
+    assert torch.equal(pq["dq"], dq), "probing dQ instance differs from the timed one"
+    assert torch.equal(pk["dk"], dk) and torch.equal(pk["dv"], dv), "probing dK/dV instance differs from the timed one"
+    for who, p in (("dQ kernel", pq), ("dK/dV kernel", pk)):
+        rs, ra = U.to64(p["rowsum"]), U.to64(p["rowabs"])
+        ratio = np.abs(rs) / np.maximum(ra, 1e-300)
+        _log(f"   row sums ({who}): max |sum dS| / sum |P dP| = {float(ratio.max()):.2e}, "
+             f"mean {float(ratio.mean()):.2e} over {rs.size} rows")
+        assert np.all(np.abs(rs) <= U.ROWSUM_TOL * ra), f"{who}: row-sum ratio max {float(ratio.max()):.3e}"
+    del pq, pk
 
-    # oracle on the last batch entry and KV group, one query head per process
+    # oracle on the last batch entry and KV group
     b, g = B - 1, Hkv - 1
     sel = U.select_group(inputs, w, b, g)
     shp = A.Shape(1, 1, 1, L, w.d_qk, w.d_v, bool(w.causal), shape.sigma)
-    rows = _rows(L, tail, nblocks)
+    rows, key0 = _rows(L, CASES[name])
+    parts = _split(rows, max(1, WORKERS // G))
     t0 = time.perf_counter()
     k64, v64 = U.to64(sel["k"]), U.to64(sel["v"])
     qh = [U.to64(sel["q"][:, j:j + 1]) for j in range(G)]
     dh = [U.to64(sel["do"][:, j:j + 1]) for j in range(G)]
     ctx = multiprocessing.get_context("spawn")
-    with cf.ProcessPoolExecutor(max_workers=min(G, 16, os.cpu_count() or 1), mp_context=ctx) as ex:
-        futs = [ex.submit(U.oracle_head_chain, qh[j], k64, v64, dh[j], shp, rows) for j in range(G)]
-        heads = [fu.result() for fu in futs]
-    _log(f"   oracle {time.perf_counter() - t0:.1f} s on rows {rows} of {G} head(s)")
-    cat = lambda get: np.concatenate([get(h) for h in heads], axis=1)       # noqa: E731
-    f = {n: cat(lambda h, n=n: h["fwd"][n]) for n in ("o", "lse", "r_o", "b_o", "b_lse")}
-    d, derr = cat(lambda h: h["delta"]), cat(lambda h: h["derr"])
-    r = {n: cat(lambda h, n=n: h["bwd"][n]) for n in ("dq", "r_dq", "b_dq")}
+    with cf.ProcessPoolExecutor(max_workers=min(WORKERS, G * len(parts)), mp_context=ctx) as ex:
+        futs = {ex.submit(_oracle_part, qh[j], k64, v64, dh[j], shp, part, key0, i == 0): (j, i)
+                for j in range(G) for i, part in enumerate(parts)}
+        res = {}
+        pending = set(futs)
+        while pending:
+            done, pending = cf.wait(pending, timeout=30)
+            for fu in done:
+                res[futs[fu]] = fu.result()
+            _log(f"   oracle: {len(res)} of {len(futs)} parts after {time.perf_counter() - t0:.0f} s")
+    _log(f"   oracle {time.perf_counter() - t0:.1f} s on rows {rows} of {G} head(s), {len(parts)} part(s) each")
+
+    idx = np.concatenate([np.arange(a, c) for a, c in rows])
+    pos = {int(r): n for n, r in enumerate(idx)}
+    nrow = len(idx)
+    f = {n: np.full((1, G, nrow) + (() if n in ("lse", "b_lse") else (w.d_v,)), np.nan)
+         for n in ("o", "r_o", "b_o", "lse", "b_lse")}
+    d, derr = np.full((1, G, nrow), np.nan), np.full((1, G, nrow), np.nan)
+    r = {n: np.full((1, G, nrow, w.d_qk), np.nan) for n in ("dq", "r_dq", "b_dq")}
+    nk = L - key0
     for n in ("dk", "dv", "r_dk", "b_dk", "r_dv", "b_dv"):
-        r[n] = sum(h["bwd"][n] for h in heads)                 # GQA: summed over the group's heads
+        r[n] = np.zeros((1, 1, nk, w.d_qk if n.endswith("dk") else w.d_v))
+    for (j, i), part in res.items():
+        sl = np.array([pos[int(x)] for x in part["idx"]])
+        for n in f:
+            f[n][0, j, sl] = part[n]
+        d[0, j, sl], derr[0, j, sl] = part["delta"], part["derr"]
+        for n in ("dq", "r_dq", "b_dq"):
+            r[n][0, j, sl] = part[n]
+        for n in ("dk", "dv", "r_dk", "b_dk", "r_dv", "b_dv"):
+            r[n][0, 0] += part[n]                              # summed over row ranges and the group's heads
+    assert not np.isnan(d).any()
+
     hs = slice(g * G, (g + 1) * G)
     L32 = (L + 31) // 32 * 32
-    for n in heads[0]["qops"]:
+    for n in res[(0, 0)]["qops"]:
         if n[0] in "qd":                                       # q_*, do_*: per query head
-            codes = np.concatenate([h["qops"][n][0] for h in heads], axis=1)
-            scales = np.concatenate([h["qops"][n][1] for h in heads], axis=1)
+            codes = np.concatenate([res[(j, 0)]["qops"][n][0] for j in range(G)], axis=1)
+            scales = np.concatenate([res[(j, 0)]["qops"][n][1] for j in range(G)], axis=1)
             hsel = hs
         else:                                                  # k_*, v_*: the KV head
-            codes, scales = heads[0]["qops"][n]
+            codes, scales = res[(0, 0)]["qops"][n]
             hsel = slice(g, g + 1)
         gc = ops[n].codes[b:b + 1, hsel].cpu().numpy()
         gs = ops[n].scales[b:b + 1, hsel].cpu().numpy().astype(np.float64)
@@ -126,18 +209,21 @@ def test_fullsize_chain_sampled(name):
         assert np.array_equal(gc, codes), n + " codes"
         assert np.array_equal(gs, scales), n + " scales"
 
-    gsl = (slice(b, b + 1), hs)
-    U.compare("O", o[gsl], f["o"], allow=f["r_o"] + f["b_o"], norm_rel=U.NORM_TOL, flip=f["r_o"])
-    U.compare("LSE", lse[gsl], f["lse"], allow=f["b_lse"], rel=0.0)
-    U.compare("delta", delta[gsl], d, allow=derr, rel=0.0)
-    _log("   ", U.compare("dq", dq[gsl], r["dq"], allow=r["r_dq"] + r["b_dq"], norm_rel=U.NORM_TOL, flip=r["r_dq"]))
-    keys = np.zeros((1, 1, L, 1), dtype=bool)
-    keys[:, :, L - tail:] = True
-    ksl = (slice(b, b + 1), slice(g, g + 1))
+    ti = torch.from_numpy(idx).cuda()
+    pick = lambda t: t[b:b + 1, hs].index_select(2, ti)        # noqa: E731
+    U.compare("O", pick(o), f["o"], allow=f["r_o"] + f["b_o"], norm_rel=U.NORM_TOL, flip=f["r_o"])
+    U.compare("LSE", pick(lse), f["lse"], allow=f["b_lse"], rel=0.0)
+    U.compare("delta", pick(delta), d, allow=derr, rel=0.0)
+    _log("   ", U.compare("dq", pick(dq), r["dq"], allow=r["r_dq"] + r["b_dq"], norm_rel=U.NORM_TOL, flip=r["r_dq"]))
     for n in ("dk", "dv"):
-        t = dk if n == "dk" else dv
-        _log("   ", U.compare(n, t[ksl], r[n], allow=r["r_" + n] + r["b_" + n], norm_rel=U.NORM_TOL, flip=r["r_" + n],
-                              mask=np.broadcast_to(keys, r[n].shape)))
+        t = (dk if n == "dk" else dv)[b:b + 1, g:g + 1, key0:]
+        _log("   ", U.compare(n, t, r[n], allow=r["r_" + n] + r["b_" + n], norm_rel=U.NORM_TOL, flip=r["r_" + n]))
+        if key0 == 0:
+            # the first key tile on its own: its workgroup walks every query step of every head
+            first = slice(0, 128)
+            _log("   ", U.compare(n + "[keys<128]", t[:, :, first], r[n][:, :, first],
+                                  allow=(r["r_" + n] + r["b_" + n])[:, :, first], norm_rel=U.NORM_TOL,
+                                  flip=r["r_" + n][:, :, first]))
 
 
 @pytest.mark.parametrize("name", ["gqa_4k", "gqa_8k"])

@@ -7,7 +7,13 @@ Bar (per tensor): FP8 codes and scales bit-exact.  O, dQ, dK, dV: norm-wise
 first-order radius of in-kernel casts whose exact input lies within the
 kernel's error budget of a rounding or scale boundary (both casts are correct
 there).  LSE and delta within their error bounds.  Under Delta-Matching
-|sum_j dS_ij| <= 1e-5 sum_j |P_ij dP_ij| on the kernel's own pre-cast dS.
+|sum_j dS_ij| <= 1e-5 sum_j |P_ij dP_ij| on the kernel's own pre-cast dS, for the
+dS of both backward kernels (dQ and dK/dV).
+
+The probing instances of the two backward kernels run the arithmetic of the timed
+ones: wherever a test uses the probes it also runs the timed instances and
+requires bit-identical dQ, dK and dV, so every comparison below covers the
+kernels bench.py times.
 """
 import functools
 import sys
@@ -79,6 +85,26 @@ def _gpu_ops(inputs):
 
 def _f32(x):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+def _timed_instances_and_dkdv_probes(shape, ops, lse, delta, g):
+    """Run the timed (probe-free) backward instances on the same inputs as the probing call
+    ``g`` and require its exact bits; return the dK/dV kernel's own row-sum probes."""
+    api = _api()
+    plain = api.attn_bwd_dq(shape, ops, lse, delta)
+    pk = api.attn_bwd_dkdv(shape, ops, lse, delta, probe=True)
+    torch.cuda.synchronize()
+    assert torch.equal(plain["dq"], g["dq"]), "probing dQ instance differs from the timed one"
+    assert torch.equal(pk["dk"], g["dk"]) and torch.equal(pk["dv"], g["dv"]), \
+        "probing dK/dV instance differs from the timed one"
+    return pk
+
+
+def _assert_zero_rowsums(p, what):
+    rs, ra = U.to64(p["rowsum"]), U.to64(p["rowabs"])
+    ratio = np.abs(rs) / np.maximum(ra, 1e-300)
+    _log(f"   {what}: max |sum_j dS_ij| / sum_j |P dP| = {float(ratio.max()):.2e}")
+    assert np.all(np.abs(rs) <= U.ROWSUM_TOL * ra), (what, float(ratio.max()))
 
 
 # ---------------------------------------------------------------------------
@@ -180,15 +206,18 @@ def test_bwd_parity(name, mode):
     api = _api()
     _, ops = _gpu_ops(inputs)
     r = ref[mode]
-    g = api.attn_bwd(shape, ops, _f32(ref["fwd"]["lse"]), _f32(r["delta"]), probe=True)
+    lse32, d32 = _f32(ref["fwd"]["lse"]), _f32(r["delta"])
+    g = api.attn_bwd(shape, ops, lse32, d32, probe=True)
     torch.cuda.synchronize()
+    pk = _timed_instances_and_dkdv_probes(shape, ops, lse32, d32, g)
     b = r["bwd"]
     for n in ("dq", "dk", "dv"):
         s = U.compare(n, g[n], b[n], allow=b["r_" + n] + b["b_" + n], norm_rel=U.NORM_TOL, flip=b["r_" + n])
         _log(f"   {s}")
-    # the probe's pre-cast row sums follow the oracle's within the kernel's error bound
-    U.compare("rowsum", g["rowsum"], b["rowsum"], allow=b["b_rowsum"] + 1e-30, rel=0.0)
-    U.compare("rowabs", g["rowabs"], b["rowabs"], allow=b["b_rowsum"] + 1e-30, rel=0.0)
+    # both kernels' pre-cast row sums follow the oracle's within the kernel's error bound
+    for who, p in (("dq", g), ("dkdv", pk)):
+        U.compare(who + " rowsum", p["rowsum"], b["rowsum"], allow=b["b_rowsum"] + 1e-30, rel=0.0)
+        U.compare(who + " rowabs", p["rowabs"], b["rowabs"], allow=b["b_rowsum"] + 1e-30, rel=0.0)
 
 
 @pytest.mark.parametrize("name", list(SMALL))
@@ -207,8 +236,9 @@ def test_chain_matched_rowsums_and_parity(name):
     b = A.backward(ref["ops"], shp, f["lse"], r["delta"], radius=True, delta_err=derr, lse_err=f["b_lse"])
     for n in ("dq", "dk", "dv"):
         _log("   ", U.compare(n, g[n], b[n], allow=b["r_" + n] + b["b_" + n], norm_rel=U.NORM_TOL, flip=b["r_" + n]))
-    rs, ra = U.to64(g["rowsum"]), U.to64(g["rowabs"])
-    assert np.all(np.abs(rs) <= U.ROWSUM_TOL * ra), float(np.max(np.abs(rs) / np.maximum(ra, 1e-300)))
+    pk = _timed_instances_and_dkdv_probes(shape, ops, g["lse"], g["delta"], g)
+    _assert_zero_rowsums(g, "dQ kernel")
+    _assert_zero_rowsums(pk, "dK/dV kernel")
     # the row sums after the E5M2 cast along keys (the third probe)
     api = _api()
     pc = api.attn_bwd_dq(shape, ops, g["lse"], g["delta"], probe_cast=True)
@@ -251,8 +281,9 @@ def test_chain_query_groups_and_softmax_scale(name):
     b = A.backward(ref["ops"], shp, f["lse"], r["delta"], radius=True, delta_err=derr, lse_err=f["b_lse"])
     for n in ("dq", "dk", "dv"):
         _log("   ", U.compare(n, g[n], b[n], allow=b["r_" + n] + b["b_" + n], norm_rel=U.NORM_TOL, flip=b["r_" + n]))
-    rs, ra = U.to64(g["rowsum"]), U.to64(g["rowabs"])
-    assert np.all(np.abs(rs) <= U.ROWSUM_TOL * ra), float(np.max(np.abs(rs) / np.maximum(ra, 1e-300)))
+    pk = _timed_instances_and_dkdv_probes(shape, ops, g["lse"], g["delta"], g)
+    _assert_zero_rowsums(g, "dQ kernel")
+    _assert_zero_rowsums(pk, "dK/dV kernel")
 
 
 @pytest.mark.parametrize("mode", ["stale", "do_matched"])
@@ -354,6 +385,9 @@ def test_short_and_ragged_lengths(L, dims):
                    lse_err=f["b_lse"])
     for n in ("dq", "dk", "dv"):
         U.compare(n, g[n], b[n], allow=b["r_" + n] + b["b_" + n], norm_rel=U.NORM_TOL, flip=b["r_" + n])
+    pk = _timed_instances_and_dkdv_probes(shape, ops, g["lse"], g["delta"], g)
+    _assert_zero_rowsums(g, "dQ kernel")
+    _assert_zero_rowsums(pk, "dK/dV kernel")
     # causal row 0 sees only key 0: O_0 is the decoded V row (P^' = 1 exactly; P' and l are 1 to
     # within the FP32 rounding of exp2(fma(s, c2, -round(mu c2))), a few ulp)
     v0 = ref["ops"]["v_s"][0, 0, 0]
@@ -383,6 +417,7 @@ def test_zero_inputs_and_zero_queries():
     _, ops = _gpu_ops(inputs)
     g = api.fwd_delta_bwd(shape, ops, "matched", probe=True)
     torch.cuda.synchronize()
+    _timed_instances_and_dkdv_probes(shape, ops, g["lse"], g["delta"], g)
     vs = A.decode_operands({"v_s": A.quantize_sequence(U.to64(inputs["v"]), "e4m3")}, 200)["v_s"][0, 0]
     n = np.arange(1, 201)[:, None]
     mean = np.cumsum(vs, axis=0) / n
@@ -393,5 +428,8 @@ def test_zero_inputs_and_zero_queries():
     _, zops = _gpu_ops(zero)
     gz = api.fwd_delta_bwd(shape, zops, "matched", probe=True)
     torch.cuda.synchronize()
+    pz = _timed_instances_and_dkdv_probes(shape, zops, gz["lse"], gz["delta"], gz)
     for n in ("o", "delta", "dq", "dk", "dv"):
         assert torch.count_nonzero(gz[n]) == 0, n
+    for n in ("rowsum", "rowabs"):
+        assert torch.count_nonzero(gz[n]) == 0 and torch.count_nonzero(pz[n]) == 0, n

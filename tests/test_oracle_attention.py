@@ -367,3 +367,68 @@ def test_postcast_rowsum_is_the_sum_of_the_e5m2_cast(causal):
     assert np.all(np.abs(u["rowsum_cast"] - u["rowsum"]) <= 1e-14 * u["rowabs"])
     assert np.all(np.abs(r["rowsum"]) <= 1e-12 * r["rowabs"])
     assert np.median(np.abs(r["rowsum_cast"]) / r["rowabs"]) > 1e-6   # the cast leaves a residual
+
+
+def _torch_block_cast(x, fmax, dtype):
+    """Cast x [..., 32 * nb] in blocks of 32 along the last axis through torch's float8 type, each
+    block scaled by the smallest power of two 2^k (k in [-126, 127]) with amax <= fmax * 2^k."""
+    blocks = x.reshape(x.shape[:-1] + (x.shape[-1] // 32, 32))
+    amax = np.abs(blocks).max(axis=-1)
+    kexp = np.where(amax > 0, np.ceil(np.log2(np.maximum(amax, 1e-300) / fmax)), -126).clip(-126, 127)
+    kexp = np.where((amax > 0) & (amax <= fmax * np.exp2(kexp - 1)), kexp - 1, kexp)
+    scale = np.exp2(kexp)[..., None]
+    cast = torch.from_numpy(blocks / scale).to(dtype).to(torch.float64).numpy() * scale
+    return cast.reshape(x.shape)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("L,r0", [(200, 0), (200, 96), (96, 0)])
+def test_query_axis_casts_brute_force(causal, L, r0):
+    """dV and dK use P and dS cast along the *query* axis: for every key column, 32-query blocks
+    (a ragged last block zero-padded).  Recomputed here from independently formed P = exp(S - LSE)
+    and the oracle's pre-cast dS through torch's float8_e4m3fn / float8_e5m2 casts (block scales
+    from their definition): dV = P^<q>^T dO^<s>, dK = sigma dS^<q>^T Q^<s> over rows [r0, L).  A cast
+    along keys instead, or a wrongly padded tail block, changes them (checked)."""
+    rng = np.random.default_rng(40 + L + r0)
+    B, Hq, Hkv, d = 1, 1, 1, 64
+    # peaked rows (scores of several units): block maxima spread over many binades, so the
+    # block scales differ between the two axes
+    q = 3.0 * rng.standard_normal((B, Hq, L, d))
+    q, k, v, do, ops = _rand_ops(rng, B, Hq, Hkv, L, d, d, q=q)
+    shp = _shape(B, Hq, Hkv, L, d, d, causal)
+    f = A.forward(ops, shp)
+    dm = A.delta(ops, shp, "matched", lse=f["lse"])
+    oh = {n: ops[n][0, 0] for n in ("q_c", "k_c", "v_c", "do_c", "q_s", "k_s", "do_s")}
+    lse = f["lse"][0, 0, r0:L]
+    r = A.backward_rows(oh, lse, dm[0, 0, r0:L], shp.sigma, causal, r0, L, keep_ds=True)
+    # P from its definition, independently of the oracle's backward
+    S = shp.sigma * (oh["q_c"][r0:L] @ oh["k_c"].T)
+    if causal:
+        S = np.where(np.arange(L)[None, :] > np.arange(r0, L)[:, None], -np.inf, S)
+    P = np.exp(S - lse[:, None])
+    n = L - r0
+    n32 = (n + 31) // 32 * 32
+    padP = np.zeros((n32, L))
+    padP[:n] = P
+    padS = np.zeros((n32, L))
+    padS[:n] = r["ds"]
+    # per key column: blocks of 32 consecutive queries (cast along axis 0 = transpose, last axis)
+    Pq = _torch_block_cast(padP.T, 448.0, torch.float8_e4m3fn).T[:n]
+    dSq = _torch_block_cast(padS.T, 57344.0, torch.float8_e5m2).T[:n]
+    dv = Pq.T @ oh["do_s"][r0:L]
+    dk = shp.sigma * (dSq.T @ oh["q_s"][r0:L])
+    np.testing.assert_allclose(r["dv"], dv, rtol=1e-12, atol=1e-14 * np.abs(dv).max())
+    np.testing.assert_allclose(r["dk"], dk, rtol=1e-12, atol=1e-14 * np.abs(dk).max())
+    # the same casts along keys give different gradients (so the test tells the axes apart)
+    Lk = (L + 31) // 32 * 32
+    padK = np.zeros((n, Lk))
+    padK[:, :L] = P
+    Pk = _torch_block_cast(padK, 448.0, torch.float8_e4m3fn)[:, :L]
+    assert np.abs(Pk.T @ oh["do_s"][r0:L] - r["dv"]).max() > 1e-6 * np.abs(dv).max()
+    # and a tail block padded with anything but zeros (here 2, above every probability) changes
+    # dV when the last block is ragged
+    if n % 32:
+        bad = padP.copy()
+        bad[n:] = 2.0
+        Pb = _torch_block_cast(bad.T, 448.0, torch.float8_e4m3fn).T[:n]
+        assert not np.allclose(Pb.T @ oh["do_s"][r0:L], dv, rtol=1e-12, atol=0)
