@@ -93,18 +93,26 @@ def _grid_exponent(a: np.ndarray, fmt: Format) -> np.ndarray:
     return np.maximum(e - 1, fmt.emin)
 
 
+def _pow2(k: np.ndarray) -> np.ndarray:
+    """2.0**k for integer k in the FP64 normal range, built from the exponent field."""
+    return ((np.asarray(k, dtype=np.int64) + 1023) << 52).view(np.float64)
+
+
 def round_to_grid(v: np.ndarray, fmt) -> np.ndarray:
-    """Nearest FP8 value of v (ties to even), as FP64.  Requires |v| <= Fmax."""
+    """Nearest FP8 value of v (ties to even), as FP64.  Requires |v| <= Fmax.
+
+    The grid step at |v| is 2^(u - mbits), u the binade exponent of |v| (never below
+    the format's emin, where the subnormals share one step); |v| / step is scaled by
+    an exact power of two and rounded half-to-even."""
     fmt = fmt_of(fmt)
     v = np.asarray(v, dtype=np.float64)
     a = np.abs(v)
     if np.any(a > fmt.fmax):
         raise ValueError("value outside the format's finite range")
-    u = _grid_exponent(a, fmt)
-    step_exp = u - fmt.mbits
-    q = np.rint(np.ldexp(a, -step_exp))          # exact; np.rint rounds half to even
-    r = np.ldexp(q, step_exp)
-    return np.copysign(r, v)
+    # unbiased FP64 exponent field of a (FP64 zeros and subnormals give -1023 and so emin)
+    u = np.maximum((a.view(np.int64) >> 52) - 1023, fmt.emin)
+    q = np.rint(a * _pow2(fmt.mbits - u))         # exact scaling; np.rint rounds half to even
+    return np.copysign(q * _pow2(u - fmt.mbits), v)
 
 
 def encode(v: np.ndarray, fmt) -> np.ndarray:
@@ -216,15 +224,21 @@ def cast_lastaxis(x: np.ndarray, fmt, err: np.ndarray | None = None):
     flag = k_lo != k_hi
     n_block = int(np.count_nonzero(flag))
     if n_block:
+        # every scale 2^kk with k_lo <= kk <= k_hi of a flagged block is a possible kernel
+        # scale: take the largest change any of them gives (block by block, kk = k_lo + o)
         idx = np.nonzero(flag)
         xf, ef, df = xb[idx], eb[idx], dec[idx]
+        klo, khi = k_lo[idx], k_hi[idx]
         worst = np.zeros_like(xf)
-        for kk in range(int(k_lo[idx].min()), int(k_hi[idx].max()) + 1):
-            use = ((k_lo[idx] <= kk) & (kk <= k_hi[idx]))[:, None]
-            sa = np.ldexp(1.0, kk)
-            for cand in (_cast_with_scale(xf - ef, sa, fmt), _cast_with_scale(xf, sa, fmt),
-                         _cast_with_scale(xf + ef, sa, fmt)):
-                worst = np.where(use, np.maximum(worst, np.abs(cand - df)), worst)
+        for o in range(int((khi - klo).max()) + 1):
+            use = np.nonzero(klo + o <= khi)[0]             # blocks with a candidate at this offset
+            sa = np.ldexp(1.0, klo[use] + o)[:, None]
+            xu, eu, du = xf[use], ef[use], df[use]
+            w = worst[use]
+            for cand in (_cast_with_scale(xu - eu, sa, fmt), _cast_with_scale(xu, sa, fmt),
+                         _cast_with_scale(xu + eu, sa, fmt)):
+                w = np.maximum(w, np.abs(cand - du))
+            worst[use] = w
         dd = delta[idx]
         delta[idx] = np.maximum(dd, worst)
     return dec.reshape(x.shape), delta.reshape(x.shape), n_elem, n_block

@@ -11,7 +11,11 @@ and within it
     tiles, whose workgroups walk every query step of every head of the group;
   * at 64K: O, LSE, delta and dQ on sampled 32-row blocks and on the last 4096
     rows, and dK, dV on the last 4096 keys (under causal masking only rows at or
-    after a key reach it, so those rows determine the keys completely).
+    after a key reach it, so those rows determine the keys completely).  The
+    64K accumulation chains of the first key tiles (2048 chained instructions
+    per dK/dV element) are covered by the instruction measurement in
+    tests/test_gpu_mfma_accumulation.py, whose error does not grow with the
+    chain.
 The same elementwise and norm-wise bars as the small-size tests apply.  On every
 row of the full problem, the matched-mode row sums |sum_j dS_ij| <= 1e-5
 sum_j |P_ij dP_ij| are checked from the probes of both backward kernels (a
