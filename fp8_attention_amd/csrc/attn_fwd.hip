@@ -222,7 +222,9 @@ __global__ __launch_bounds__((64 * fwd_waves<DQK, DV>())) void fwd_kernel(
     const float mx = fmaxf(fmaxf(bm[0], bm[1]), fmaxf(bm[2], bm[3]));
     const float mu_new = fmaxf(mu, mx);
     const float m2 = (mu_new == -INFINITY) ? 0.f : mu_new * c2;
-    const float alpha = __builtin_amdgcn_exp2f(mu * c2 - m2);
+    // exactly 1 when no maximum moved (the fused mu*c2 - m2 would otherwise leave the
+    // product's rounding error, and an exp2 of it that can miss 1 by an ulp)
+    const float alpha = mu_new == mu ? 1.f : __builtin_amdgcn_exp2f(mu * c2 - m2);
     mu = mu_new;
     l *= (double)alpha;
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
