@@ -143,6 +143,10 @@ def main():
     dq = torch.empty((B, Hq, L, w.d_qk), dtype=torch.float32, device="cuda")
     dk = torch.empty((B, w.heads_kv, L, w.d_qk), dtype=torch.float32, device="cuda")
     dv = torch.empty((B, w.heads_kv, L, w.d_v), dtype=torch.float32, device="cuda")
+    # dK/dV workspace for the head split of small grids (none at the long-context sizes)
+    ws_bytes = api.dkdv_workspace_size(shape)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") if ws_bytes else None
+    _log(f"[bench] dK/dV head-split workspace {ws_bytes} bytes")
 
     def step(ev=None):
         if ev is not None:
@@ -154,7 +158,7 @@ def main():
                        lse=lse, out=delta)
         if ev is not None:
             ev[2].record()
-        api.attn_bwd_dkdv(shape, ops, lse, delta, dk=dk, dv=dv)
+        api.attn_bwd_dkdv_ws(shape, ops, lse, delta, workspace=ws, dk=dk, dv=dv)
         if ev is not None:
             ev[3].record()
         api.attn_bwd_dq(shape, ops, lse, delta, dq=dq)

@@ -11,7 +11,7 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdm.so")
 
-DM_OK, DM_ERR_NULL, DM_ERR_SHAPE, DM_ERR_ALIGN, DM_ERR_ENUM, DM_ERR_HIP = range(6)
+DM_OK, DM_ERR_NULL, DM_ERR_SHAPE, DM_ERR_ALIGN, DM_ERR_ENUM, DM_ERR_HIP, DM_ERR_WORKSPACE = range(7)
 DM_E4M3, DM_E5M2 = 0, 1
 DM_BF16, DM_F32 = 0, 1
 DM_AXIS_COLS, DM_AXIS_ROWS = 0, 1
@@ -19,7 +19,8 @@ DM_DELTA_STALE, DM_DELTA_DO_MATCHED, DM_DELTA_MATCHED = 0, 1, 2
 
 # every symbol include/dm_attn.h declares
 EXPORTS = ("dm_padded_len", "dm_status_string", "dm_quantize_blockfp8", "dm_attn_fwd", "dm_attn_delta",
-           "dm_attn_bwd", "dm_attn_bwd_dkdv", "dm_attn_bwd_dkdv_probes", "dm_attn_bwd_dq", "dm_attn_bwd_dq_probes")
+           "dm_attn_bwd", "dm_attn_bwd_dkdv", "dm_attn_bwd_dkdv_workspace_size", "dm_attn_bwd_dkdv_ws",
+           "dm_attn_bwd_dkdv_probes", "dm_attn_bwd_dq", "dm_attn_bwd_dq_probes")
 DM_MAX_SEQLEN = 1 << 24
 
 
@@ -66,6 +67,10 @@ def load() -> ctypes.CDLL:
     lib.dm_attn_bwd.restype = i32
     lib.dm_attn_bwd_dkdv.argtypes = [sp] + [Operand] * 6 + [vp] * 4 + [vp]
     lib.dm_attn_bwd_dkdv.restype = i32
+    lib.dm_attn_bwd_dkdv_workspace_size.argtypes = [sp, ctypes.POINTER(i64)]
+    lib.dm_attn_bwd_dkdv_workspace_size.restype = i32
+    lib.dm_attn_bwd_dkdv_ws.argtypes = [sp] + [Operand] * 6 + [vp] * 5 + [i64, vp]
+    lib.dm_attn_bwd_dkdv_ws.restype = i32
     lib.dm_attn_bwd_dkdv_probes.argtypes = [sp] + [Operand] * 6 + [vp] * 6 + [vp]
     lib.dm_attn_bwd_dkdv_probes.restype = i32
     lib.dm_attn_bwd_dq.argtypes = [sp] + [Operand] * 5 + [vp] * 5 + [vp]

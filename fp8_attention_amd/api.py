@@ -15,6 +15,7 @@ from typing import NamedTuple, Optional
 import torch
 
 from . import _lib
+from ._lib import DmError  # noqa: F401  (raised by every call on a non-zero status)
 
 MODES = {"stale": _lib.DM_DELTA_STALE, "do_matched": _lib.DM_DELTA_DO_MATCHED, "matched": _lib.DM_DELTA_MATCHED}
 FORMATS = {"e4m3": _lib.DM_E4M3, "e5m2": _lib.DM_E5M2}
@@ -268,6 +269,43 @@ def attn_bwd_dkdv(shape: AttnShape, ops: dict, lse: torch.Tensor, delta: torch.T
         st = _lib.load().dm_attn_bwd_dkdv(*args, _stream(lse))
         _lib.check(st, "dm_attn_bwd_dkdv")
     return out
+
+
+def dkdv_workspace_size(shape: AttnShape) -> int:
+    """dm_attn_bwd_dkdv_workspace_size: bytes of workspace ``attn_bwd_dkdv_ws`` needs (0: none)."""
+    n = ctypes.c_int64(0)
+    cs = shape.c()
+    _lib.check(_lib.load().dm_attn_bwd_dkdv_workspace_size(ctypes.byref(cs), ctypes.byref(n)),
+               "dm_attn_bwd_dkdv_workspace_size")
+    return int(n.value)
+
+
+def attn_bwd_dkdv_ws(shape: AttnShape, ops: dict, lse: torch.Tensor, delta: torch.Tensor,
+                     workspace: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                     dv: Optional[torch.Tensor] = None) -> dict:
+    """dm_attn_bwd_dkdv_ws -> {"dk","dv"}: dK/dV with the query heads of a KV group split over
+    several workgroups when the grid is small (partial sums in ``workspace``, a device uint8
+    tensor of at least ``dkdv_workspace_size(shape)`` bytes; allocated here when None)."""
+    _need_bwd(shape, ops, ("q_c", "q_s", "k_c", "v_c", "do_c", "do_s"), lse, delta, dk=dk, dv=dv)
+    dev = lse.device
+    B, Hkv, L = shape.batch, shape.heads_kv, shape.seqlen
+    if dk is None:
+        dk = torch.empty((B, Hkv, L, shape.d_qk), dtype=torch.float32, device=dev)
+    if dv is None:
+        dv = torch.empty((B, Hkv, L, shape.d_v), dtype=torch.float32, device=dev)
+    if workspace is None:
+        need = dkdv_workspace_size(shape)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+    if workspace is not None and (workspace.device != dev or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on the operands' device")
+    wp = workspace.data_ptr() if workspace is not None else None
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    cs = shape.c()
+    st = _lib.load().dm_attn_bwd_dkdv_ws(ctypes.byref(cs), ops["q_c"].c(), ops["q_s"].c(), ops["k_c"].c(),
+                                         ops["v_c"].c(), ops["do_c"].c(), ops["do_s"].c(), lse.data_ptr(),
+                                         delta.data_ptr(), dk.data_ptr(), dv.data_ptr(), wp, wb, _stream(lse))
+    _lib.check(st, "dm_attn_bwd_dkdv_ws")
+    return {"dk": dk, "dv": dv}
 
 
 def attn_bwd_dq(shape: AttnShape, ops: dict, lse: torch.Tensor, delta: torch.Tensor, probe: bool = False,

@@ -72,6 +72,7 @@ const char* dm_status_string(dm_status s) {
     case DM_ERR_ALIGN: return "DM_ERR_ALIGN: a pointer is not 16-byte aligned";
     case DM_ERR_ENUM: return "DM_ERR_ENUM: an enum argument is out of range";
     case DM_ERR_HIP: return "DM_ERR_HIP: the HIP runtime reported an error";
+    case DM_ERR_WORKSPACE: return "DM_ERR_WORKSPACE: the workspace is smaller than this shape needs";
   }
   return "unknown dm_status";
 }
@@ -157,6 +158,37 @@ dm_status dm_attn_bwd_dkdv(const dm_attn_shape* shape, dm_fp8_operand q_c, dm_fp
   if (shape->seqlen == 0) return DM_OK;
   return hip_status(dm::launch_dkdv(dims_of(shape), op(q_c), op(q_s), op(k_c), op(v_c), op(do_c), op(do_s), lse,
                                     delta, dk, dv, nullptr, nullptr, stream));
+}
+
+dm_status dm_attn_bwd_dkdv_workspace_size(const dm_attn_shape* shape, int64_t* bytes) {
+  if (bytes == nullptr) return DM_ERR_NULL;
+  dm_status st = check_shape(shape);
+  if (st != DM_OK) return st;
+  const dm::AttnDims d = dims_of(shape);
+  *bytes = shape->seqlen == 0 ? 0 : dm::dkdv_d128_workspace_bytes(d, dm::dkdv_head_split(d));
+  return DM_OK;
+}
+
+dm_status dm_attn_bwd_dkdv_ws(const dm_attn_shape* shape, dm_fp8_operand q_c, dm_fp8_operand q_s, dm_fp8_operand k_c,
+                              dm_fp8_operand v_c, dm_fp8_operand do_c, dm_fp8_operand do_s, const float* lse,
+                              const float* delta, float* dk, float* dv, void* workspace, int64_t workspace_bytes,
+                              hipStream_t stream) {
+  dm_status st = check_shape(shape);
+  if (st != DM_OK) return st;
+  const dm_fp8_operand ops[6] = {q_c, q_s, k_c, v_c, do_c, do_s};
+  for (const auto& x : ops)
+    if ((st = check_operand(x)) != DM_OK) return st;
+  if ((st = check_ptrs({lse, delta, dk, dv})) != DM_OK) return st;
+  if (shape->seqlen == 0) return DM_OK;
+  const dm::AttnDims d = dims_of(shape);
+  const int64_t need = dm::dkdv_d128_workspace_bytes(d, dm::dkdv_head_split(d));
+  if (need > 0) {
+    if (workspace == nullptr) return DM_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return DM_ERR_ALIGN;
+    if (workspace_bytes < need) return DM_ERR_WORKSPACE;
+  }
+  return hip_status(dm::launch_dkdv_split(d, op(q_c), op(q_s), op(k_c), op(v_c), op(do_c), op(do_s), lse, delta, dk,
+                                          dv, static_cast<float*>(workspace), stream));
 }
 
 dm_status dm_attn_bwd_dkdv_probes(const dm_attn_shape* shape, dm_fp8_operand q_c, dm_fp8_operand q_s,

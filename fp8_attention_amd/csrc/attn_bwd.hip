@@ -8,7 +8,8 @@ hipError_t launch_dkdv(const AttnDims& d, Operand qc, Operand qs, Operand kc, Op
                        const float* lse, const float* delta, float* dk, float* dv, double* ps, double* pa,
                        hipStream_t s) {
   if (d.dqk == 64 && d.dv == 64) return launch_dkdv_t<64, 64>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, ps, pa, s);
-  if (d.dqk == 128 && d.dv == 128) return launch_dkdv_d128(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, ps, pa, s);
+  if (d.dqk == 128 && d.dv == 128)
+    return launch_dkdv_d128(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, ps, pa, nullptr, 1, s);
   if (d.dqk == 192 && d.dv == 128)
     return launch_dkdv_t<192, 128>(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, ps, pa, s);
   if (d.dqk == 64 && d.dv == 128)
@@ -20,6 +21,16 @@ hipError_t launch_dkdv(const AttnDims& d, Operand qc, Operand qs, Operand kc, Op
   if (d.dqk == 256 && d.dv == 256)
     return launch_dkdv_256_256(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, ps, pa, s);
   return hipErrorInvalidValue;
+}
+
+int dkdv_head_split(const AttnDims& d) { return d.dqk == 128 && d.dv == 128 ? dkdv_d128_head_split(d) : 1; }
+
+hipError_t launch_dkdv_split(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand vc, Operand doc,
+                             Operand dos, const float* lse, const float* delta, float* dk, float* dv, float* ws,
+                             hipStream_t s) {
+  const int hs = dkdv_head_split(d);
+  if (hs == 1) return launch_dkdv(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, nullptr, nullptr, s);
+  return launch_dkdv_d128(d, qc, qs, kc, vc, doc, dos, lse, delta, dk, dv, nullptr, nullptr, ws, hs, s);
 }
 
 hipError_t launch_bwd(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand ks, Operand vc, Operand doc,

@@ -23,6 +23,11 @@
 // all at once, they stall the waves behind them); LSE and delta come through registers.  One barrier per step.  dK and dV accumulate in
 // registers over every query head of the group and are written once.
 //
+// Head split (small grids): with HS > 1 the G query heads of a KV group are dealt to
+// HS workgroups per key tile (heads [hp*G/HS, (hp+1)*G/HS)), so a grid of one key tile
+// per CU still spreads its long causal tiles; each part writes its raw dV^T and dK^T
+// sums to a workspace and dkdv_reduce_kernel adds the parts in a fixed order.
+//
 // The PROBE instance runs the same arithmetic and also returns, per query row,
 // the sum over keys of the FP32 dS it casts and of |P dP^| (section 03 of the
 // Delta-Matching project page: matched delta makes the rows of dS sum to zero up
@@ -66,17 +71,20 @@ __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
     const uint8_t* __restrict__ vc, const float* __restrict__ vcs, const uint8_t* __restrict__ doc,
     const float* __restrict__ docs, const uint8_t* __restrict__ dos, const float* __restrict__ doss,
     const float* __restrict__ lse, const float* __restrict__ delta, float* __restrict__ dk, float* __restrict__ dv,
-    double* __restrict__ psum, double* __restrict__ pabs, int Hq, int Hkv, int L, int Lp, float sigma) {
+    double* __restrict__ psum, double* __restrict__ pabs, float* __restrict__ part, int HS, int Hq, int Hkv, int L,
+    int Lp, float sigma) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kSTAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int n = lane & 15, g = lane >> 4;              // key column / lane group of the 16x16 tiles
   const int nkt = Lp / kKT;
-  const int nhb = Hkv * (int)(gridDim.x / (nkt * Hkv));    // Hkv * B
+  const int nhb = Hkv * (int)(gridDim.x / (nkt * Hkv * HS));    // Hkv * B
   const int hk = (int)blockIdx.x % nhb % Hkv, b = (int)blockIdx.x % nhb / Hkv;
-  const int k0 = ((int)blockIdx.x / nhb) * kKT;           // key tiles slowest: long causal tiles first
+  const int rest = (int)blockIdx.x / nhb;                 // key tile (slowest: long causal tiles first), head part
+  const int k0 = (rest / HS) * kKT, hp = rest % HS;
   const int G = Hq / Hkv;
+  const int hbeg = hp * (G / HS), hend = hbeg + G / HS;  // this workgroup's query heads of the group
   const int kw0 = k0 + 16 * w;                       // this wave's first key
   const int key = kw0 + n;                           // this lane's key
   const int LB = Lp / kBlock;
@@ -167,8 +175,8 @@ __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
   const int qstart = CAUSAL ? k0 : 0;
   const int nsteps = (Lp - qstart) / kQT;
   uint8_t* const stage0 = lds;
-  issue(sources(qhead0, qstart), stage0);
-  load_small(qhead0, qstart);
+  issue(sources(qhead0 + hbeg, qstart), stage0);
+  load_small(qhead0 + hbeg, qstart);
   store_small(stage0);
 
   // LDS read offsets of this lane's operand row (row n of a 16-row tile, chunks g and 4+g)
@@ -185,7 +193,7 @@ __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
     wait_vmem();
     __syncthreads();                               // step it staged; the other buffer is free
     const bool head_end = i + 1 == nsteps;
-    const bool more = !(head_end && hh + 1 == G);
+    const bool more = !(head_end && hh + 1 == hend);
     const int64_t nqh = qhead0 + hh + (head_end && more ? 1 : 0);
     const int nq0 = !more ? q0 : head_end ? qstart : q0 + kQT;
     const Src nx = sources(nqh, nq0);
@@ -310,7 +318,7 @@ __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
   // per head: the diagonal step for causal (all steps when the tile holds padded
   // keys) with the mask, then the rest in a loop without mask code
   const int nmask = (k0 + kKT > L) ? nsteps : (CAUSAL ? 1 : 0);
-  for (int hh = 0, it = 0; hh < G; ++hh) {
+  for (int hh = hbeg, it = 0; hh < hend; ++hh) {
     for (int i = 0; i < nmask; ++i, ++it) step(it, hh, i, std::true_type{});
     for (int i = nmask; i < nsteps; ++i, ++it) step(it, hh, i, std::false_type{});
   }
@@ -318,25 +326,74 @@ __global__ __launch_bounds__(kNT) void dkdv_d128_kernel(
   wait_vmem();                                     // the last step's (unused) loads
   // ---- dK, dV written once per key: lane (n, g), register i of tile ct <-> channel 16ct + 4g + i
   if (key < L) {
-    float* dkr = dk + (khead * L + key) * kD + 4 * g;
-    float* dvr = dv + (khead * L + key) * kD + 4 * g;
+    if (HS == 1) {
+      float* dkr = dk + (khead * L + key) * kD + 4 * g;
+      float* dvr = dv + (khead * L + key) * kD + 4 * g;
 #pragma unroll
-    for (int ct = 0; ct < kD / 16; ++ct) {
-      *reinterpret_cast<v4f*>(dvr + 16 * ct) = accv[ct];
-      *reinterpret_cast<v4f*>(dkr + 16 * ct) = sigma * acck[ct];
+      for (int ct = 0; ct < kD / 16; ++ct) {
+        *reinterpret_cast<v4f*>(dvr + 16 * ct) = accv[ct];
+        *reinterpret_cast<v4f*>(dkr + 16 * ct) = sigma * acck[ct];
+      }
+    } else {
+      // part hp: [B*Hkv][L][dV^T sums (128) | dK^T sums (128)], unscaled
+      float* pr = part + (((int64_t)hp * nhb + khead) * L + key) * (2 * kD) + 4 * g;
+#pragma unroll
+      for (int ct = 0; ct < kD / 16; ++ct) {
+        *reinterpret_cast<v4f*>(pr + 16 * ct) = accv[ct];
+        *reinterpret_cast<v4f*>(pr + kD + 16 * ct) = acck[ct];
+      }
     }
   }
 }
 
+// dV = sum of the HS parts' dV^T sums, dK = sigma * sum of their dK^T sums, parts added in
+// order 0, 1, ... (deterministic).  One thread per 4 channels of one key row.
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* __restrict__ part, float* __restrict__ dk,
+                                                         float* __restrict__ dv, int64_t nrows, int HS,
+                                                         float sigma) {
+  const int64_t n4 = nrows * (kD / 4);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = i / (kD / 4);
+    const int c = (int)(i % (kD / 4)) * 4;
+    v4f sv = *reinterpret_cast<const v4f*>(part + row * (2 * kD) + c);
+    v4f sk = *reinterpret_cast<const v4f*>(part + row * (2 * kD) + kD + c);
+    for (int p = 1; p < HS; ++p) {
+      const float* pr = part + ((int64_t)p * nrows + row) * (2 * kD);
+      sv += *reinterpret_cast<const v4f*>(pr + c);
+      sk += *reinterpret_cast<const v4f*>(pr + kD + c);
+    }
+    *reinterpret_cast<v4f*>(dv + row * kD + c) = sv;
+    *reinterpret_cast<v4f*>(dk + row * kD + c) = sigma * sk;
+  }
+}
+
+int dkdv_d128_head_split(const AttnDims& d) {
+  // deal the heads of a KV group to more workgroups while the grid is under
+  // kSplitTarget workgroups (four per CU of MI355X's 256; one workgroup of this
+  // kernel's LDS size runs on a CU at a time).  The grid stays under 2 * kSplitTarget,
+  // so the partial sums take under 2 * kSplitTarget * 128 KiB = 256 MiB.
+  constexpr int64_t kSplitTarget = 1024;
+  const int G = d.Hq / d.Hkv;
+  const int64_t nwg = (int64_t)(d.Lp / kKT) * d.Hkv * d.B;
+  int hs = 1;
+  while (G % (2 * hs) == 0 && nwg * hs < kSplitTarget) hs *= 2;
+  return hs;
+}
+
+int64_t dkdv_d128_workspace_bytes(const AttnDims& d, int hs) {
+  return hs > 1 ? (int64_t)hs * d.B * d.Hkv * d.L * 2 * kD * (int64_t)sizeof(float) : 0;
+}
+
 hipError_t launch_dkdv_d128(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand vc, Operand doc,
                             Operand dos, const float* lse, const float* delta, float* dk, float* dv, double* ps,
-                            double* pa, hipStream_t s) {
+                            double* pa, float* ws, int hs, hipStream_t s) {
   if (d.dqk != kD || d.dv != kD || d.Lp % kKT != 0 || (ps == nullptr) != (pa == nullptr)) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)(d.Lp / kKT) * d.Hkv * d.B);
+  if (hs < 1 || (d.Hq / d.Hkv) % hs != 0 || (hs > 1 && (ws == nullptr || ps != nullptr))) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(d.Lp / kKT) * d.Hkv * d.B * hs);
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, dim3(kNT), 0, s, qc.codes, qc.scales, qs.codes, qs.scales, kc.codes, kc.scales,
                        vc.codes, vc.scales, doc.codes, doc.scales, dos.codes, dos.scales, lse, delta, dk, dv, ps, pa,
-                       d.Hq, d.Hkv, d.L, d.Lp, d.sigma);
+                       ws, hs, d.Hq, d.Hkv, d.L, d.Lp, d.sigma);
   };
   if (ps) {
     // the probe rows are sums over every key tile: start them from zero
@@ -349,6 +406,13 @@ hipError_t launch_dkdv_d128(const AttnDims& d, Operand qc, Operand qs, Operand k
   } else {
     if (d.causal) go(dkdv_d128_kernel<true, false>);
     else go(dkdv_d128_kernel<false, false>);
+    if (hs > 1) {
+      const int64_t nrows = (int64_t)d.B * d.Hkv * d.L;
+      int64_t blocks = (nrows * (kD / 4) + 255) / 256;
+      if (blocks > 4096) blocks = 4096;
+      hipLaunchKernelGGL(dkdv_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, ws, dk, dv, nrows, hs,
+                         d.sigma);
+    }
   }
   return hipGetLastError();
 }

@@ -37,10 +37,23 @@ hipError_t launch_dkdv(const AttnDims& d, Operand qc, Operand qs, Operand kc, Op
                        const float* lse, const float* delta, float* dk, float* dv, double* ps, double* pa,
                        hipStream_t s);
 
-// d_qk = d_v = 128 form of launch_dkdv (attn_dkdv128.hip)
+// d_qk = d_v = 128 form of launch_dkdv (attn_dkdv128.hip).  hs > 1 deals the query heads of
+// each KV group to hs workgroups per key tile, with their partial sums in ws
+// (dkdv_d128_workspace_bytes(d, hs) bytes) and a reduction kernel after; hs must divide
+// Hq / Hkv and excludes the probes.
 hipError_t launch_dkdv_d128(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand vc, Operand doc,
                             Operand dos, const float* lse, const float* delta, float* dk, float* dv, double* ps,
-                            double* pa, hipStream_t s);
+                            double* pa, float* ws, int hs, hipStream_t s);
+// head split the d = 128 kernel takes for a shape (1: none) and its workspace bytes
+int dkdv_d128_head_split(const AttnDims& d);
+int64_t dkdv_d128_workspace_bytes(const AttnDims& d, int hs);
+// the head split launch_dkdv_split uses for d (1 for head dims without a split form)
+int dkdv_head_split(const AttnDims& d);
+// launch_dkdv with the head split dkdv_head_split(d) and its partial sums in ws
+// (dkdv_d128_workspace_bytes(d, dkdv_head_split(d)) bytes; may be null when that is 0)
+hipError_t launch_dkdv_split(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand vc, Operand doc,
+                             Operand dos, const float* lse, const float* delta, float* dk, float* dv, float* ws,
+                             hipStream_t s);
 // d_qk = d_v = 256 form of launch_dkdv (attn_dkdv_wide.hip)
 hipError_t launch_dkdv_256_256(const AttnDims& d, Operand qc, Operand qs, Operand kc, Operand vc, Operand doc,
                                Operand dos, const float* lse, const float* delta, float* dk, float* dv, double* ps,

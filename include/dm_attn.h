@@ -69,7 +69,8 @@ typedef enum {
   DM_ERR_SHAPE = 2,  /* unsupported or inconsistent sizes */
   DM_ERR_ALIGN = 3,  /* a pointer is not 16-byte aligned */
   DM_ERR_ENUM = 4,   /* an enum argument is out of range */
-  DM_ERR_HIP = 5     /* the HIP runtime reported an error at launch */
+  DM_ERR_HIP = 5,    /* the HIP runtime reported an error at launch */
+  DM_ERR_WORKSPACE = 6 /* a workspace is smaller than the shape needs */
 } dm_status;
 
 typedef enum { DM_E4M3 = 0, DM_E5M2 = 1 } dm_fp8_format;
@@ -186,6 +187,31 @@ dm_status dm_attn_bwd_dq(const dm_attn_shape* shape, dm_fp8_operand q_c, dm_fp8_
                          dm_fp8_operand k_s, dm_fp8_operand v_c, dm_fp8_operand do_c,
                          const float* lse, const float* delta, float* dq,
                          double* probe_rowsum_ds, double* probe_rowsum_abs_pdp, hipStream_t stream);
+
+/*
+ * dm_attn_bwd_dkdv for grids too small to fill the chip (section 03's dK and dV
+ * products, as for dm_attn_bwd_dkdv).  The dK/dV kernel keeps one tile of keys
+ * and sums over every query head of its KV group; when the shape has too few key
+ * tiles to occupy every compute unit several times over, the query heads of each
+ * KV group are dealt to 2, 4, ... workgroups per key tile, each writes its partial
+ * dK and dV sums to the workspace, and a second kernel adds the parts in a fixed
+ * order.  Results are deterministic; they may differ from dm_attn_bwd_dkdv's in
+ * the last bits (FP32 sums taken in another order) and meet the same accuracy.
+ *   dm_attn_bwd_dkdv_workspace_size: *bytes (host pointer) = the workspace the
+ *     shape needs; 0 when it takes no split (head dims other than d_qk = d_v =
+ *     128, or grids that are already large).  Depends on the shape only and is
+ *     under 256 MiB for every shape.
+ *   dm_attn_bwd_dkdv_ws: workspace is a device buffer of workspace_bytes bytes,
+ *     16-byte aligned, owned by the caller, contents undefined on entry and on
+ *     return (NULL allowed when the size is 0).  DM_ERR_WORKSPACE when
+ *     workspace_bytes is below the size; other errors as for dm_attn_bwd.  Calls
+ *     that share a workspace must not overlap.
+ */
+dm_status dm_attn_bwd_dkdv_workspace_size(const dm_attn_shape* shape, int64_t* bytes);
+dm_status dm_attn_bwd_dkdv_ws(const dm_attn_shape* shape, dm_fp8_operand q_c, dm_fp8_operand q_s,
+                              dm_fp8_operand k_c, dm_fp8_operand v_c, dm_fp8_operand do_c,
+                              dm_fp8_operand do_s, const float* lse, const float* delta, float* dk,
+                              float* dv, void* workspace, int64_t workspace_bytes, hipStream_t stream);
 
 /*
  * dm_attn_bwd_dkdv with the row-sum probes of the dS that the dK/dV kernel itself

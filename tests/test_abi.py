@@ -40,7 +40,7 @@ def test_padded_len_and_strings():
     lib = _lib.load()
     assert [lib.dm_padded_len(x) for x in (0, 1, 128, 129, 65536)] == [0, 128, 128, 256, 65536]
     assert lib.dm_padded_len(-1) == -1
-    for s in range(6):
+    for s in range(7):
         assert _lib.status_string(s).startswith("DM_")
     assert "unknown" in _lib.status_string(99)
 
@@ -154,6 +154,52 @@ def test_split_backward_validation():
     assert kp(ctypes.byref(s), *[op] * 6, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == _lib.DM_ERR_SHAPE
     assert lib.dm_attn_bwd_dkdv(ctypes.byref(s), *[op] * 6, FAKE, FAKE, FAKE, FAKE, None) == _lib.DM_ERR_SHAPE
     assert lib.dm_attn_bwd_dq(ctypes.byref(s), *[op] * 5, FAKE, FAKE, FAKE, None, None, None) == _lib.DM_ERR_SHAPE
+
+
+def _expected_split_bytes(B, Hq, Hkv, L, d_qk, d_v):
+    """The head-split policy as documented: d_qk = d_v = 128 only; the query heads of a KV group
+    are dealt to 2, 4, ... workgroups per 128-key tile while the grid has fewer than 1024
+    workgroups and the split divides the group; partial dK and dV sums of 4 bytes per channel."""
+    if (d_qk, d_v) != (128, 128) or L == 0:
+        return 0
+    G, nwg, hs = Hq // Hkv, -(-L // 128) * Hkv * B, 1
+    while G % (2 * hs) == 0 and nwg * hs < 1024:
+        hs *= 2
+    return 0 if hs == 1 else hs * B * Hkv * L * (d_qk + d_v) * 4
+
+
+@pytest.mark.parametrize("dims", [(2, 16, 4, 4096, 128, 128), (4, 32, 8, 8192, 128, 128), (1, 16, 4, 65536, 128, 128),
+                                  (1, 8, 1, 192, 128, 128), (1, 4, 2, 320, 128, 128), (1, 6, 2, 1000, 128, 128),
+                                  (1, 1, 1, 1, 128, 128), (3, 64, 1, 128, 128, 128), (1, 8, 8, 100, 128, 128),
+                                  (2, 16, 4, 4096, 256, 256), (2, 16, 16, 4096, 192, 128), (1, 4, 1, 0, 128, 128)])
+def test_head_split_workspace_size(dims):
+    lib = _lib.load()
+    s = AttnShape(*dims, True).c()
+    n = ctypes.c_int64(-1)
+    assert lib.dm_attn_bwd_dkdv_workspace_size(ctypes.byref(s), ctypes.byref(n)) == _lib.DM_OK
+    assert n.value == _expected_split_bytes(*dims), (dims, n.value)
+    assert n.value < 256 << 20
+    assert lib.dm_attn_bwd_dkdv_workspace_size(ctypes.byref(s), None) == _lib.DM_ERR_NULL
+    assert lib.dm_attn_bwd_dkdv_workspace_size(None, ctypes.byref(n)) == _lib.DM_ERR_NULL
+    s.d_v = 96
+    assert lib.dm_attn_bwd_dkdv_workspace_size(ctypes.byref(s), ctypes.byref(n)) == _lib.DM_ERR_SHAPE
+
+
+def test_head_split_entry_validation():
+    lib = _lib.load()
+    s = AttnShape(2, 16, 4, 4096, 128, 128, True).c()
+    n = ctypes.c_int64(0)
+    lib.dm_attn_bwd_dkdv_workspace_size(ctypes.byref(s), ctypes.byref(n))
+    need = n.value
+    assert need == 4 * 2 * 4 * 4096 * 256 * 4
+    op = _op()
+    ws = lib.dm_attn_bwd_dkdv_ws
+    assert ws(ctypes.byref(s), *[op] * 6, FAKE, FAKE, FAKE, FAKE, None, need, None) == _lib.DM_ERR_NULL
+    assert ws(ctypes.byref(s), *[op] * 6, FAKE, FAKE, FAKE, FAKE, MIS, need, None) == _lib.DM_ERR_ALIGN
+    assert ws(ctypes.byref(s), *[op] * 6, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == _lib.DM_ERR_WORKSPACE
+    assert ws(ctypes.byref(s), *[op] * 6, FAKE, FAKE, FAKE, None, FAKE, need, None) == _lib.DM_ERR_NULL
+    s.d_qk = 96
+    assert ws(ctypes.byref(s), *[op] * 6, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == _lib.DM_ERR_SHAPE
 
 
 def test_quantize_validation():

@@ -22,6 +22,10 @@ sum_j |P_ij dP_ij| are checked from the probes of both backward kernels (a
 property that needs no oracle), and the probing instances are required to give
 the timed instances' dQ, dK and dV bit for bit.
 
+Where the shape's dK/dV grid is small enough for the head-split entry
+(dm_attn_bwd_dkdv_ws, the call bench.py times) to split, the unsplit kernel's dK
+and dV are compared as well.
+
 The oracle runs in up to 16 spawned processes (one BLAS thread each): every
 query head of the group split into row ranges; dK and dV are summed over the
 ranges and heads.
@@ -132,16 +136,22 @@ def test_fullsize_chain_sampled(name):
     api.attn_fwd(shape, ops["q_c"], ops["k_c"], ops["v_s"], o=o, lse=lse)
     api.attn_delta(shape, "matched", do_c=ops["do_c"], q_c=ops["q_c"], k_c=ops["k_c"], v_c=ops["v_c"],
                    lse=lse, out=delta)
-    api.attn_bwd_dkdv(shape, ops, lse, delta, dk=dk, dv=dv)
+    need = api.dkdv_workspace_size(shape)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+    api.attn_bwd_dkdv_ws(shape, ops, lse, delta, workspace=ws, dk=dk, dv=dv)
     api.attn_bwd_dq(shape, ops, lse, delta, dq=dq)
     # the row-sum probes of both backward kernels over the whole problem; the probing
     # instances must reproduce the timed ones bit for bit
     pq = api.attn_bwd_dq(shape, ops, lse, delta, probe=True)
     pk = api.attn_bwd_dkdv(shape, ops, lse, delta, probe=True)
+    # a small grid takes the head split in the timed step; then the unsplit kernel (whose
+    # arithmetic the probing instance repeats) is checked as well
+    unsplit = api.attn_bwd_dkdv(shape, ops, lse, delta) if need else {"dk": dk, "dv": dv}
     torch.cuda.synchronize()
-    _log("   gpu done")
+    _log("   gpu done" + (f"; timed dK/dV with the head split ({need >> 20} MiB workspace)" if need else ""))
     assert torch.equal(pq["dq"], dq), "probing dQ instance differs from the timed one"
-    assert torch.equal(pk["dk"], dk) and torch.equal(pk["dv"], dv), "probing dK/dV instance differs from the timed one"
+    assert torch.equal(pk["dk"], unsplit["dk"]) and torch.equal(pk["dv"], unsplit["dv"]), \
+        "probing dK/dV instance differs from the unsplit timed one"
     for who, p in (("dQ kernel", pq), ("dK/dV kernel", pk)):
         rs, ra = U.to64(p["rowsum"]), U.to64(p["rowabs"])
         ratio = np.abs(rs) / np.maximum(ra, 1e-300)
@@ -219,13 +229,17 @@ def test_fullsize_chain_sampled(name):
     U.compare("LSE", pick(lse), f["lse"], allow=f["b_lse"], rel=0.0)
     U.compare("delta", pick(delta), d, allow=derr, rel=0.0)
     _log("   ", U.compare("dq", pick(dq), r["dq"], allow=r["r_dq"] + r["b_dq"], norm_rel=U.NORM_TOL, flip=r["r_dq"]))
-    for n in ("dk", "dv"):
-        t = (dk if n == "dk" else dv)[b:b + 1, g:g + 1, key0:]
-        _log("   ", U.compare(n, t, r[n], allow=r["r_" + n] + r["b_" + n], norm_rel=U.NORM_TOL, flip=r["r_" + n]))
+    outs = [("dk", "dk", dk), ("dv", "dv", dv)]
+    if need:
+        outs += [(n + " (unsplit)", n, unsplit[n]) for n in ("dk", "dv")]
+    for label, n, full in outs:
+        t = full[b:b + 1, g:g + 1, key0:]
+        _log("   ", U.compare(label, t, r[n], allow=r["r_" + n] + r["b_" + n], norm_rel=U.NORM_TOL,
+                              flip=r["r_" + n]))
         if key0 == 0:
             # the first key tile on its own: its workgroup walks every query step of every head
             first = slice(0, 128)
-            _log("   ", U.compare(n + "[keys<128]", t[:, :, first], r[n][:, :, first],
+            _log("   ", U.compare(label + "[keys<128]", t[:, :, first], r[n][:, :, first],
                                   allow=(r["r_" + n] + r["b_" + n])[:, :, first], norm_rel=U.NORM_TOL,
                                   flip=r["r_" + n][:, :, first]))
 

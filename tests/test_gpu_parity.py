@@ -286,6 +286,68 @@ def test_chain_query_groups_and_softmax_scale(name):
     _assert_zero_rowsums(pk, "dK/dV kernel")
 
 
+# shapes for the head-split dK/dV entry, with the split each takes: the query heads of a KV
+# group dealt to hs workgroups per key tile (1: no split, no workspace)
+HEAD_SPLIT_CASES = {
+    "gqa_ragged": 2, "gqa_gain": 4, "mqa_d128_s0.25": 8, "tiny": 1, "mla": 1, "d256": 1,
+}
+
+
+def _split_case(name):
+    if name in GROUP_SCALE_CASES:
+        w, scale = GROUP_SCALE_CASES[name]
+        api = _api()
+        shape = api.AttnShape(w.batch, w.heads_q, w.heads_kv, w.seqlen, w.d_qk, w.d_v, w.causal, scale)
+        shp = U.oracle_shape(w, shape.sigma)
+        inputs = W.generate(w)
+        _log(f"[oracle] {name}")
+        return w, inputs, shape, shp, U.run_oracle(inputs, shp, modes=("matched",))
+    return _case(name)
+
+
+@pytest.mark.parametrize("name", list(HEAD_SPLIT_CASES))
+def test_head_split_dkdv_parity(name):
+    """dm_attn_bwd_dkdv_ws: dK, dV against the oracle (matched delta) with the split's partial sums
+    in a workspace that holds garbage on entry; bit-identical on a second call; identical to
+    dm_attn_bwd_dkdv where the shape takes no split."""
+    w, inputs, shape, shp, ref = _split_case(name)
+    api = _api()
+    hs = HEAD_SPLIT_CASES[name]
+    need = api.dkdv_workspace_size(shape)
+    assert need == (0 if hs == 1 else hs * w.batch * w.heads_kv * w.seqlen * 2 * w.d_qk * 4), need
+    _log(f"[head split] {name}: {need} bytes of workspace")
+    _, ops = _gpu_ops(inputs)
+    r = ref["matched"]
+    lse32, d32 = _f32(ref["fwd"]["lse"]), _f32(r["delta"])
+    ws = torch.full((max(need, 16) + 256,), 0xFF, dtype=torch.uint8, device="cuda")   # NaN bytes
+    g1 = api.attn_bwd_dkdv_ws(shape, ops, lse32, d32, workspace=ws)
+    g2 = api.attn_bwd_dkdv_ws(shape, ops, lse32, d32, workspace=ws[:max(need, 16)])
+    plain = api.attn_bwd_dkdv(shape, ops, lse32, d32)
+    torch.cuda.synchronize()
+    b = r["bwd"]
+    for n in ("dk", "dv"):
+        _log("   ", U.compare(n, g1[n], b[n], allow=b["r_" + n] + b["b_" + n], norm_rel=U.NORM_TOL,
+                              flip=b["r_" + n]))
+        assert torch.equal(g1[n], g2[n]), n + ": head-split result differs between two calls"
+        if hs == 1:
+            assert torch.equal(g1[n], plain[n]), n + ": without a split the result must be dm_attn_bwd_dkdv's"
+
+
+def test_head_split_workspace_errors():
+    api = _api()
+    w, inputs, shape, shp, ref = _case("gqa_gain")
+    _, ops = _gpu_ops(inputs)
+    lse32, d32 = _f32(ref["fwd"]["lse"]), _f32(ref["matched"]["delta"])
+    need = api.dkdv_workspace_size(shape)
+    assert need > 0
+    ws = torch.empty(need - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(api.DmError, match="DM_ERR_WORKSPACE"):
+        api.attn_bwd_dkdv_ws(shape, ops, lse32, d32, workspace=ws)
+    ws = torch.empty(need + 32, dtype=torch.uint8, device="cuda")
+    with pytest.raises(api.DmError, match="DM_ERR_ALIGN"):
+        api.attn_bwd_dkdv_ws(shape, ops, lse32, d32, workspace=ws[8:])
+
+
 @pytest.mark.parametrize("mode", ["stale", "do_matched"])
 @pytest.mark.parametrize("name", ["gqa_ragged", "mla", "d256"])
 def test_chain_saved_output_modes(name, mode):
