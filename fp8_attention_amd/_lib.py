@@ -20,8 +20,10 @@ DM_DELTA_STALE, DM_DELTA_DO_MATCHED, DM_DELTA_MATCHED = 0, 1, 2
 # every symbol include/dm_attn.h declares
 EXPORTS = ("dm_padded_len", "dm_status_string", "dm_quantize_blockfp8", "dm_attn_fwd", "dm_attn_delta",
            "dm_attn_bwd", "dm_attn_bwd_dkdv", "dm_attn_bwd_dkdv_workspace_size", "dm_attn_bwd_dkdv_ws",
+           "dm_attn_bwd_dkdv_noalloc",
            "dm_attn_bwd_dkdv_probes", "dm_attn_bwd_dq", "dm_attn_bwd_dq_probes")
 DM_MAX_SEQLEN = 1 << 24
+DM_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class Operand(ctypes.Structure):
@@ -71,6 +73,8 @@ def load() -> ctypes.CDLL:
     lib.dm_attn_bwd_dkdv_workspace_size.restype = i32
     lib.dm_attn_bwd_dkdv_ws.argtypes = [sp] + [Operand] * 6 + [vp] * 5 + [i64, vp]
     lib.dm_attn_bwd_dkdv_ws.restype = i32
+    lib.dm_attn_bwd_dkdv_noalloc.argtypes = [sp] + [Operand] * 6 + [vp] * 4 + [vp]
+    lib.dm_attn_bwd_dkdv_noalloc.restype = i32
     lib.dm_attn_bwd_dkdv_probes.argtypes = [sp] + [Operand] * 6 + [vp] * 6 + [vp]
     lib.dm_attn_bwd_dkdv_probes.restype = i32
     lib.dm_attn_bwd_dq.argtypes = [sp] + [Operand] * 5 + [vp] * 5 + [vp]

@@ -308,6 +308,20 @@ def attn_bwd_dkdv_ws(shape: AttnShape, ops: dict, lse: torch.Tensor, delta: torc
     return {"dk": dk, "dv": dv}
 
 
+def attn_bwd_dkdv_noalloc(shape: AttnShape, ops: dict, lse: torch.Tensor, delta: torch.Tensor,
+                          dk: torch.Tensor, dv: torch.Tensor) -> dict:
+    """dm_attn_bwd_dkdv_noalloc -> {"dk","dv"}: ``attn_bwd_dkdv_ws`` with the library's fixed
+    per-device scratch instead of a workspace; the outputs are the caller's (nothing is
+    allocated here or in the library).  Calls that overlap on one device race."""
+    _need_bwd(shape, ops, ("q_c", "q_s", "k_c", "v_c", "do_c", "do_s"), lse, delta, dk=dk, dv=dv)
+    cs = shape.c()
+    st = _lib.load().dm_attn_bwd_dkdv_noalloc(ctypes.byref(cs), ops["q_c"].c(), ops["q_s"].c(), ops["k_c"].c(),
+                                              ops["v_c"].c(), ops["do_c"].c(), ops["do_s"].c(), lse.data_ptr(),
+                                              delta.data_ptr(), dk.data_ptr(), dv.data_ptr(), _stream(lse))
+    _lib.check(st, "dm_attn_bwd_dkdv_noalloc")
+    return {"dk": dk, "dv": dv}
+
+
 def attn_bwd_dq(shape: AttnShape, ops: dict, lse: torch.Tensor, delta: torch.Tensor, probe: bool = False,
                 dq: Optional[torch.Tensor] = None, probe_cast: bool = False) -> dict:
     """dm_attn_bwd_dq -> {"dq"} float32 (+ "rowsum","rowabs" probes): the query-stationary half.

@@ -1,12 +1,39 @@
 // C ABI of libdm: argument validation (pure host code, no HIP call before it
-// passes) and dispatch to the kernel launchers.
+// passes) and dispatch to the kernel launchers; the fixed scratch of the
+// allocation-free dK/dV call.
 #include <math.h>
 #include <stdint.h>
+
+#include <mutex>
 
 #include "dm_attn.h"
 #include "dm_internal.h"
 
+// Scratch of dm_attn_bwd_dkdv_noalloc: the head split's partial sums, for callers that
+// cannot allocate.  Each device the library runs on holds its own copy until the process
+// ends.  Host code never passes the array's name to a kernel (on the host it is only a
+// stand-in for the symbol); it uses the device address hipGetSymbolAddress returns.
+static __device__ __align__(256) uint8_t scratch[DM_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // per device; null until the first call on that device
+
+// The device address of the current device's scratch, looked up once per device (with
+// that device current).  Null on failure.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -72,7 +99,9 @@ const char* dm_status_string(dm_status s) {
     case DM_ERR_ALIGN: return "DM_ERR_ALIGN: a pointer is not 16-byte aligned";
     case DM_ERR_ENUM: return "DM_ERR_ENUM: an enum argument is out of range";
     case DM_ERR_HIP: return "DM_ERR_HIP: the HIP runtime reported an error";
-    case DM_ERR_WORKSPACE: return "DM_ERR_WORKSPACE: the workspace is smaller than this shape needs";
+    case DM_ERR_WORKSPACE:
+      return "DM_ERR_WORKSPACE: the workspace (or the fixed scratch of the allocation-free call) is smaller than "
+             "this shape needs";
   }
   return "unknown dm_status";
 }
@@ -189,6 +218,28 @@ dm_status dm_attn_bwd_dkdv_ws(const dm_attn_shape* shape, dm_fp8_operand q_c, dm
   }
   return hip_status(dm::launch_dkdv_split(d, op(q_c), op(q_s), op(k_c), op(v_c), op(do_c), op(do_s), lse, delta, dk,
                                           dv, static_cast<float*>(workspace), stream));
+}
+
+dm_status dm_attn_bwd_dkdv_noalloc(const dm_attn_shape* shape, dm_fp8_operand q_c, dm_fp8_operand q_s,
+                                   dm_fp8_operand k_c, dm_fp8_operand v_c, dm_fp8_operand do_c, dm_fp8_operand do_s,
+                                   const float* lse, const float* delta, float* dk, float* dv, hipStream_t stream) {
+  dm_status st = check_shape(shape);
+  if (st != DM_OK) return st;
+  const dm_fp8_operand ops[6] = {q_c, q_s, k_c, v_c, do_c, do_s};
+  for (const auto& x : ops)
+    if ((st = check_operand(x)) != DM_OK) return st;
+  if ((st = check_ptrs({lse, delta, dk, dv})) != DM_OK) return st;
+  if (shape->seqlen == 0) return DM_OK;
+  const dm::AttnDims d = dims_of(shape);
+  const int64_t need = dm::dkdv_d128_workspace_bytes(d, dm::dkdv_head_split(d));
+  if (need > (int64_t)DM_NOALLOC_SCRATCH_BYTES) return DM_ERR_WORKSPACE;
+  float* ws = nullptr;
+  if (need > 0) {
+    ws = static_cast<float*>(device_scratch());
+    if (ws == nullptr) return DM_ERR_HIP;
+  }
+  return hip_status(dm::launch_dkdv_split(d, op(q_c), op(q_s), op(k_c), op(v_c), op(do_c), op(do_s), lse, delta, dk,
+                                          dv, ws, stream));
 }
 
 dm_status dm_attn_bwd_dkdv_probes(const dm_attn_shape* shape, dm_fp8_operand q_c, dm_fp8_operand q_s,

@@ -19,7 +19,9 @@
  * - All pointers are device pointers, except the dm_attn_shape pointer, which
  *   is a host pointer read before the call returns.  The caller allocates and
  *   owns every buffer; the library allocates nothing and keeps no pointer
- *   after a call returns.
+ *   after a call returns.  (The one exception is the fixed device scratch of
+ *   dm_attn_bwd_dkdv_noalloc, a static array of DM_NOALLOC_SCRATCH_BYTES on
+ *   each device, and its per-device address kept from the first such call.)
  * - Every call only enqueues work on `stream` and returns.  The status covers
  *   host-side argument checks and the launch itself (hipGetLastError); a
  *   device-side fault surfaces at the caller's next synchronisation.
@@ -48,7 +50,8 @@
  *   0 <= L <= DM_MAX_SEQLEN (the kernels address up to 128 rows of one head's
  *   sequence-major operand with 32-bit offsets); L == 0 is a no-op.
  * - Pointers must be 16-byte aligned (DM_ERR_ALIGN otherwise).
- * - Calls are reentrant; the library has no global state.
+ * - Calls are reentrant; apart from that scratch the library has no global
+ *   state.
  */
 #ifndef DM_ATTN_H
 #define DM_ATTN_H
@@ -62,6 +65,9 @@ extern "C" {
 
 /* Largest supported sequence length (2^24). */
 #define DM_MAX_SEQLEN (1 << 24)
+
+/* Size of the fixed per-device scratch of dm_attn_bwd_dkdv_noalloc (128 MiB). */
+#define DM_NOALLOC_SCRATCH_BYTES (128u << 20)
 
 typedef enum {
   DM_OK = 0,
@@ -212,6 +218,29 @@ dm_status dm_attn_bwd_dkdv_ws(const dm_attn_shape* shape, dm_fp8_operand q_c, dm
                               dm_fp8_operand k_c, dm_fp8_operand v_c, dm_fp8_operand do_c,
                               dm_fp8_operand do_s, const float* lse, const float* delta, float* dk,
                               float* dv, void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dm_attn_bwd_dkdv_ws for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * head split's partial sums go to a static scratch array of
+ * DM_NOALLOC_SCRATCH_BYTES that each device holds from the library's first use
+ * of it until the process ends.  Same arguments as dm_attn_bwd_dkdv minus the
+ * workspace; dK and dV are bit for bit those of dm_attn_bwd_dkdv_ws.
+ *   - Never calls hipMalloc, hipFree or an allocating routine.  The first call on
+ *     a device looks up that device's scratch address (hipGetSymbolAddress) with
+ *     the current device; stream and buffers must belong to the current device.
+ *   - DM_ERR_WORKSPACE when dm_attn_bwd_dkdv_workspace_size exceeds
+ *     DM_NOALLOC_SCRATCH_BYTES (nothing enqueued; use dm_attn_bwd_dkdv_ws then).
+ *   - The scratch needs no clearing: every call writes every byte it reads.  All
+ *     calls on one device share it, so calls that overlap in time on one device
+ *     (other streams, other threads) race and give wrong results; serialize them.
+ *   - Other errors as for dm_attn_bwd; DM_ERR_HIP also when the scratch address
+ *     cannot be obtained.
+ */
+dm_status dm_attn_bwd_dkdv_noalloc(const dm_attn_shape* shape, dm_fp8_operand q_c, dm_fp8_operand q_s,
+                                   dm_fp8_operand k_c, dm_fp8_operand v_c, dm_fp8_operand do_c,
+                                   dm_fp8_operand do_s, const float* lse, const float* delta, float* dk,
+                                   float* dv, hipStream_t stream);
 
 /*
  * dm_attn_bwd_dkdv with the row-sum probes of the dS that the dK/dV kernel itself

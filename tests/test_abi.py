@@ -202,6 +202,28 @@ def test_head_split_entry_validation():
     assert ws(ctypes.byref(s), *[op] * 6, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == _lib.DM_ERR_SHAPE
 
 
+def test_noalloc_entry_validation():
+    """The allocation-free dK/dV call: argument errors, and a shape whose head split needs more
+    than the fixed scratch is refused before any GPU call."""
+    lib = _lib.load()
+    na = lib.dm_attn_bwd_dkdv_noalloc
+    op = _op()
+    s = AttnShape(1, 16, 8, 12288, 128, 128, True).c()      # 768 key tiles x heads: split 2, 192 MiB
+    n = ctypes.c_int64(0)
+    assert lib.dm_attn_bwd_dkdv_workspace_size(ctypes.byref(s), ctypes.byref(n)) == _lib.DM_OK
+    assert n.value == 192 << 20 > _lib.DM_NOALLOC_SCRATCH_BYTES
+    assert na(ctypes.byref(s), *[op] * 6, FAKE, FAKE, FAKE, FAKE, None) == _lib.DM_ERR_WORKSPACE
+    assert na(ctypes.byref(s), *[op] * 6, FAKE, FAKE, FAKE, None, None) == _lib.DM_ERR_NULL
+    assert na(ctypes.byref(s), *[op] * 6, FAKE, FAKE, MIS, FAKE, None) == _lib.DM_ERR_ALIGN
+    assert na(None, *[op] * 6, FAKE, FAKE, FAKE, FAKE, None) == _lib.DM_ERR_NULL
+    s.d_qk = 96
+    assert na(ctypes.byref(s), *[op] * 6, FAKE, FAKE, FAKE, FAKE, None) == _lib.DM_ERR_SHAPE
+    # the 4K GQA workload's split fits exactly
+    s = AttnShape(2, 16, 4, 4096, 128, 128, True).c()
+    assert lib.dm_attn_bwd_dkdv_workspace_size(ctypes.byref(s), ctypes.byref(n)) == _lib.DM_OK
+    assert n.value == _lib.DM_NOALLOC_SCRATCH_BYTES
+
+
 def test_quantize_validation():
     lib = _lib.load()
     q = lib.dm_quantize_blockfp8
