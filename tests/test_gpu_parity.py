@@ -289,11 +289,24 @@ def test_chain_query_groups_and_softmax_scale(name):
 # shapes for the head-split dK/dV entry, with the split each takes: the query heads of a KV
 # group dealt to hs workgroups per key tile (1: no split, no workspace)
 HEAD_SPLIT_CASES = {
-    "gqa_ragged": 2, "gqa_gain": 4, "mqa_d128_s0.25": 8, "tiny": 1, "mla": 1, "d256": 1,
+    "gqa_ragged": 2, "gqa_gain": 4, "mqa_d128_s0.25": 8, "tiny": 1, "mla": 1, "d256": 1, "gqa_nc": 4,
+}
+# non-causal, ragged: every key tile walks every query step, the last key tile is partly padding
+SPLIT_ONLY = {
+    "gqa_nc": W.small("gqa_nc", batch=1, heads_q=8, heads_kv=2, seqlen=250, d_qk=128, d_v=128, causal=False,
+                      kind="rmsnorm", seed=24),
 }
 
 
 def _split_case(name):
+    if name in SPLIT_ONLY:
+        w = SPLIT_ONLY[name]
+        api = _api()
+        shape = api.AttnShape(w.batch, w.heads_q, w.heads_kv, w.seqlen, w.d_qk, w.d_v, w.causal)
+        shp = U.oracle_shape(w, shape.sigma)
+        inputs = W.generate(w)
+        _log(f"[oracle] {name}")
+        return w, inputs, shape, shp, U.run_oracle(inputs, shp, modes=("matched",))
     if name in GROUP_SCALE_CASES:
         w, scale = GROUP_SCALE_CASES[name]
         api = _api()
