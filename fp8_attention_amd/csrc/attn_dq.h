@@ -292,6 +292,9 @@ __global__ __launch_bounds__((64 * dq_waves<DQK, DV>())) void dq_kernel(
       if (t & 1) {
         // dS^<k> of key half st complete: dQ^T += K^<s>^T dS^<k>^T over those 64 keys
         const int st = t >> 1;
+        // raised wave priority while this wave issues its dQ products, so they reach the
+        // matrix core ahead of the other wave's FP32 work (about 1% at 8K; same arithmetic)
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           const uint8_t* p = vp + C::OFF_T + 32 * ct * CK;
@@ -302,6 +305,7 @@ __global__ __launch_bounds__((64 * dq_waves<DQK, DV>())) void dq_kernel(
           else xs = x[tb + h];
           acc[ct] = mfma<E4M3, E5M2>(a, dsb[st], acc[ct], e8m0(xs), dssc[st]);
         }
+        __builtin_amdgcn_s_setprio(0);
       }
       __builtin_amdgcn_sched_barrier(0);        // one key tile in flight at a time (register budget)
     }
