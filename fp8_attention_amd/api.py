@@ -357,8 +357,11 @@ def attn_bwd_dq(shape: AttnShape, ops: dict, lse: torch.Tensor, delta: torch.Ten
 
 
 def fwd_delta_bwd(shape: AttnShape, ops: dict, mode: str = "matched", do: Optional[torch.Tensor] = None,
-                  probe: bool = False) -> dict:
-    """One pass of the whole path on already-quantized operands: forward, delta, backward."""
+                  probe: bool = False, split: bool = False) -> dict:
+    """One pass of the whole path on already-quantized operands: forward, delta, backward.
+
+    ``split``: the backward as dm_attn_bwd_dkdv_ws (head split of small grids, workspace
+    allocated here) plus dm_attn_bwd_dq instead of the fused dm_attn_bwd."""
     o, lse = attn_fwd(shape, ops["q_c"], ops["k_c"], ops["v_s"])
     if mode == "matched":
         d = attn_delta(shape, mode, do_c=ops["do_c"], q_c=ops["q_c"], k_c=ops["k_c"], v_c=ops["v_c"], lse=lse)
@@ -366,6 +369,10 @@ def fwd_delta_bwd(shape: AttnShape, ops: dict, mode: str = "matched", do: Option
         d = attn_delta(shape, mode, o=o, do_c=ops["do_c"])
     else:
         d = attn_delta(shape, mode, o=o, do=do)
-    g = attn_bwd(shape, ops, lse, d, probe=probe)
+    if split and not probe:
+        g = attn_bwd_dkdv_ws(shape, ops, lse, d)
+        g.update(attn_bwd_dq(shape, ops, lse, d))
+    else:
+        g = attn_bwd(shape, ops, lse, d, probe=probe)
     g.update(o=o, lse=lse, delta=d)
     return g

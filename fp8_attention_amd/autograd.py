@@ -94,7 +94,10 @@ class Fp8Attention(torch.autograd.Function):
             delta = api.attn_delta(shape, mode, o=o, do_c=ops["do_c"])
         else:
             delta = api.attn_delta(shape, mode, o=o, do=do)
-        g = api.attn_bwd(shape, ops, lse, delta)
+        # dK/dV through the head-split entry (a workspace only where the grid is small),
+        # then dQ: the same kernels as the fused call otherwise
+        g = api.attn_bwd_dkdv_ws(shape, ops, lse, delta)
+        g.update(api.attn_bwd_dq(shape, ops, lse, delta))
         tq, tk, tv = ctx.dtypes
         return g["dq"].to(tq), g["dk"].to(tk), g["dv"].to(tv), None, None, None
 

@@ -89,7 +89,7 @@ def test_autograd_matches_call_chain(case):
     # the same steps through the binding
     shape = api.AttnShape(B, Hq, Hkv, L, dqk, dv, causal)
     ops = api.quantize_operands(q, k, v, do)
-    g = api.fwd_delta_bwd(shape, ops, mode=mode, do=do)
+    g = api.fwd_delta_bwd(shape, ops, mode=mode, do=do, split=True)
     torch.cuda.synchronize()
     assert o.dtype == dtype and qr.grad.dtype == dtype
     assert torch.equal(o, g["o"].to(dtype))
