@@ -236,6 +236,17 @@ __global__ __launch_bounds__((64 * fwd_waves<DQK, DV>())) void fwd_kernel(
     int psc[2] = {0, 0};
     float lc = 0.f;
     const int nb = (c + 1) & 1;
+    // K^<c> operand rows of the next chunk's tiles, read one tile ahead of their
+    // products so the LDS latency hides behind this chunk's softmax (K buffer nb
+    // landed before the barrier above).  Not at d_qk = 192: its three operand
+    // pairs would spill at two waves per SIMD.
+    constexpr bool KPRE = DQK != 192;
+    v8i kpre[KPRE ? KS : 1];
+    if constexpr (KPRE) {
+      const uint8_t* sK = lds + nb * C::K;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kpre[ks] = cat(lds_read16(sK + kro[ks][0]), lds_read16(sK + kro[ks][1]));
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const float am = __builtin_amdgcn_exp2f(fmaf(bm[t], c2, -m2));
@@ -254,7 +265,20 @@ __global__ __launch_bounds__((64 * fwd_waves<DQK, DV>())) void fwd_kernel(
       if ((t & 1) == h) psc[t >> 1] = k + 127;
       // tile t of chunk c+1 into the registers just freed (computed unconditionally:
       // past this wave's last chunk the result is simply never used)
-      s[t] = score_tile(nb, t);
+      if constexpr (KPRE) {
+        const float* sKs = reinterpret_cast<const float*>(lds + C::OFF_KS + nb * C::KS) + (32 * t + kr) * KB;
+        v16f acc = v16f{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = mfma<E4M3, E4M3>(kpre[ks], qb[ks], acc, e8m0(sKs[2 * ks + h]), qsc[ks]);
+        s[t] = acc;
+        if (t + 1 < 4) {
+          const uint8_t* sK = lds + nb * C::K + 32 * (t + 1) * DQK;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) kpre[ks] = cat(lds_read16(sK + kro[ks][0]), lds_read16(sK + kro[ks][1]));
+        }
+      } else {
+        s[t] = score_tile(nb, t);
+      }
     }
 
     const uint8_t* sV = lds + C::OFF_V + (c & 1) * C::V;
