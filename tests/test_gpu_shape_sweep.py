@@ -6,7 +6,8 @@ exact multiples of the tiles), every supported head-dimension pair, the causal
 flag, the input family and sometimes an explicit softmax scale, all from one seed,
 and checks the whole matched chain -- forward (O, LSE), matched delta, dQ, dK, dV
 on the instances the benchmark runs -- plus the head-split dK/dV entry
-(dm_attn_bwd_dkdv_ws) against the oracle, with the bars of the other parity tests.
+(dm_attn_bwd_dkdv_ws) against the oracle, with the bars of the other parity tests, and
+the allocation-free entry (dm_attn_bwd_dkdv_noalloc) bit for bit against it.
 """
 import sys
 
@@ -73,7 +74,11 @@ def test_sweep_chain_and_head_split(case):
     ops = api.quantize_operands(dev["q"], dev["k"], dev["v"], dev["do"])
     g = api.fwd_delta_bwd(shape, ops, "matched")
     split = api.attn_bwd_dkdv_ws(shape, ops, g["lse"], g["delta"])
+    # the allocation-free entry: same kernels on the library's fixed scratch, same bits
+    na = {"dk": torch.empty_like(split["dk"]), "dv": torch.empty_like(split["dv"])}
+    api.attn_bwd_dkdv_noalloc(shape, ops, g["lse"], g["delta"], na["dk"], na["dv"])
     torch.cuda.synchronize()
+    assert torch.equal(na["dk"], split["dk"]) and torch.equal(na["dv"], split["dv"])
     f, r = ref["fwd"], ref["matched"]
     U.compare("O", g["o"], f["o"], allow=f["r_o"] + f["b_o"], norm_rel=U.NORM_TOL, flip=f["r_o"])
     U.compare("LSE", g["lse"], f["lse"], allow=f["b_lse"], rel=0.0)
