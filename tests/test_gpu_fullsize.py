@@ -53,6 +53,13 @@ CASES = {
     "gqa_64k": (4096, 8),
     "mla_4k": None,
     "gqa_d256_4k": None,
+    "gqa_8k_b1": None,
+}
+# the long-context head geometry at batch 1: its dK/dV grid (64 key tiles x 8 KV heads) is small
+# enough for the head split (two workgroups per key tile), so the timed call splits at 8K
+EXTRA_WORKLOADS = {
+    "gqa_8k_b1": W.small("gqa_8k_b1", batch=1, heads_q=32, heads_kv=8, seqlen=8192, d_qk=128, d_v=128,
+                         causal=True, kind="rmsnorm", q_gain7=2.0, k_gain7=5.4, seed=1006),
 }
 WORKERS = 16
 
@@ -119,7 +126,7 @@ def _oracle_part(q, k, v, do, shp, rows, key0, want_codes):
 @pytest.mark.parametrize("name", list(CASES))
 def test_fullsize_chain_sampled(name):
     from fp8_attention_amd import api
-    w = W.WORKLOADS[name]
+    w = EXTRA_WORKLOADS[name] if name in EXTRA_WORKLOADS else W.WORKLOADS[name]
     B, Hq, Hkv, L, G = w.batch, w.heads_q, w.heads_kv, w.seqlen, w.group
     _log(f"[fullsize] {name}: {w}")
     inputs = W.generate(w)
